@@ -1,0 +1,228 @@
+"""ctypes binding of libslora.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (without the
+`slora_` prefix) and does nothing but convert arguments and raise SloraError on a
+negative return code. All work runs in the library's HIP kernels and host code;
+there is no fallback of any kind: if libslora.so is missing the import fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libslora.so")
+
+OK, E_INVALID, E_POOL_FULL, E_STATE, E_HIP = 0, -1, -2, -3, -4
+F16, BF16 = 0, 1
+POLICY_AUTO, POLICY_MBGMV, POLICY_SGMV = 0, 1, 2
+DTYPES = {"f16": F16, "bf16": BF16}
+
+_c_i32, _c_i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+
+class SloraError(RuntimeError):
+    def __init__(self, code: int, what: str, msg: str):
+        super().__init__(f"{what} failed ({code}): {msg}")
+        self.code = code
+
+
+class Lora(ctypes.Structure):
+    _fields_ = [("pool", _vp), ("n_pages", _c_i64), ("page_elems", _c_i32), ("dtype", _c_i32),
+                ("d_in", _c_i32), ("d_out", _c_i32), ("page_table", _vp),
+                ("page_table_len", _c_i64), ("n_adapters", _c_i32), ("base", _vp), ("rank", _vp),
+                ("scale", _vp), ("r_max", _c_i32)]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [("n_tokens", _c_i32), ("n_segments", _c_i32), ("seg_offsets", _vp),
+                ("seg_adapter", _vp), ("token_adapter", _vp), ("policy", _c_i32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libslora.so. Raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with heterogeneous_lora_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, I = _vp, _c_i32
+    sig = {
+        "slora_last_error": ([], ctypes.c_char_p),
+        "slora_abi_version": ([], I),
+        "slora_pool_create": ([P, _c_i64, I, I, ctypes.c_uint64, P], I),
+        "slora_pool_destroy": ([P], I),
+        "slora_pool_info": ([P, P, P, P, P], I),
+        "slora_pool_alloc_kv": ([P, I, P], I),
+        "slora_pool_free_kv": ([P, P, I], I),
+        "slora_pool_alloc_adapter": ([P, I, I, I, P, P], I),
+        "slora_pool_free_adapter": ([P, I], I),
+        "slora_pool_page_table": ([P, I, I, P, _c_i64, P, P, P], I),
+        "slora_pool_owners": ([P, P], I),
+        "slora_fetch_async": ([P, I, P, P, P, P], I),
+        "slora_workspace_size": ([P, P, P], I),
+        "slora_shrink": ([P, P, P, P, P, _c_i64, P], I),
+        "slora_expand": ([P, P, P, P, P, _c_i64, P], I),
+        "slora_apply": ([P, P, P, P, P, _c_i64, P], I),
+        "slora_plan_inspect": ([P, P, P, P, I, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise SloraError(rc, what, load().slora_last_error().decode())
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def last_error() -> str:
+    return load().slora_last_error().decode()
+
+
+def abi_version() -> int:
+    return load().slora_abi_version()
+
+
+class Pool:
+    """Owner of one slora_pool handle over caller-owned device memory."""
+
+    def __init__(self, dev_ptr: int, n_pages: int, page_elems: int, dtype: str, seed: int):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        _check(self._lib.slora_pool_create(ctypes.c_void_p(dev_ptr), n_pages, page_elems,
+                                           DTYPES[dtype], seed, ctypes.byref(h)), "pool_create")
+        self.handle = h
+        self.n_pages, self.page_elems, self.dtype = n_pages, page_elems, dtype
+
+    def destroy(self):
+        if self.handle:
+            _check(self._lib.slora_pool_destroy(self.handle), "pool_destroy")
+            self.handle = None
+
+    def info(self):
+        n, f, pe, dt = _c_i64(), _c_i64(), _c_i32(), _c_i32()
+        _check(self._lib.slora_pool_info(self.handle, ctypes.byref(n), ctypes.byref(f),
+                                         ctypes.byref(pe), ctypes.byref(dt)), "pool_info")
+        return dict(n_pages=n.value, n_free=f.value, page_elems=pe.value, dtype=dt.value)
+
+    def alloc_kv(self, n: int) -> np.ndarray:
+        out = np.empty(n, np.int32)
+        _check(self._lib.slora_pool_alloc_kv(self.handle, n, _p(out)), "pool_alloc_kv")
+        return out
+
+    def free_kv(self, ids: np.ndarray):
+        ids = np.ascontiguousarray(ids, np.int32)
+        _check(self._lib.slora_pool_free_kv(self.handle, _p(ids), ids.size), "pool_free_kv")
+
+    def alloc_adapter(self, adapter_id: int, rank: int, d_in: Sequence[int], d_out: Sequence[int]):
+        di = np.ascontiguousarray(d_in, np.int32)
+        do = np.ascontiguousarray(d_out, np.int32)
+        _check(self._lib.slora_pool_alloc_adapter(self.handle, adapter_id, rank, di.size, _p(di),
+                                                  _p(do)), "pool_alloc_adapter")
+
+    def free_adapter(self, adapter_id: int):
+        _check(self._lib.slora_pool_free_adapter(self.handle, adapter_id), "pool_free_adapter")
+
+    def page_table(self, proj: int, n_adapters: int):
+        n = _c_i64()
+        base = np.empty(max(n_adapters, 1), np.int64)
+        rank = np.empty(max(n_adapters, 1), np.int32)
+        _check(self._lib.slora_pool_page_table(self.handle, proj, n_adapters, None, 0,
+                                               ctypes.byref(n), _p(base), _p(rank)), "page_table")
+        pt = np.empty(max(n.value, 1), np.int32)
+        _check(self._lib.slora_pool_page_table(self.handle, proj, n_adapters, _p(pt), pt.size,
+                                               ctypes.byref(n), _p(base), _p(rank)), "page_table")
+        return pt[:n.value], base[:n_adapters], rank[:n_adapters]
+
+    def owners(self) -> np.ndarray:
+        out = np.empty(self.n_pages, np.int32)
+        _check(self._lib.slora_pool_owners(self.handle, _p(out)), "pool_owners")
+        return out
+
+    def fetch_async(self, adapter_id: int, host_at: Sequence[int], host_b: Sequence[int],
+                    stream: int, event: Optional[int]):
+        at = (ctypes.c_void_p * max(len(host_at), 1))(*host_at)
+        b = (ctypes.c_void_p * max(len(host_b), 1))(*host_b)
+        _check(self._lib.slora_fetch_async(self.handle, adapter_id, at, b, ctypes.c_void_p(stream),
+                                           ctypes.c_void_p(event) if event else None),
+               "fetch_async")
+
+
+class Call:
+    """Host-side arguments of one compute call (keeps the host arrays alive)."""
+
+    def __init__(self, *, pool_ptr: int, n_pages: int, page_elems: int, dtype: str, d_in: int,
+                 d_out: int, page_table_ptr: int, page_table_len: int, base: np.ndarray,
+                 rank: np.ndarray, scale: np.ndarray, r_max: int, n_tokens: int,
+                 seg_offsets: np.ndarray, seg_adapter: np.ndarray, token_adapter: np.ndarray,
+                 policy: int = POLICY_AUTO):
+        self.base = np.ascontiguousarray(base, np.int64)
+        self.rank = np.ascontiguousarray(rank, np.int32)
+        self.scale = np.ascontiguousarray(scale, np.float32)
+        self.seg_offsets = np.ascontiguousarray(seg_offsets, np.int32)
+        self.seg_adapter = np.ascontiguousarray(seg_adapter, np.int32)
+        self.token_adapter = np.ascontiguousarray(token_adapter, np.int32)
+        self.lora = Lora(pool=pool_ptr, n_pages=n_pages, page_elems=page_elems,
+                         dtype=DTYPES[dtype], d_in=d_in, d_out=d_out, page_table=page_table_ptr,
+                         page_table_len=page_table_len, n_adapters=self.rank.size,
+                         base=self.base.ctypes.data, rank=self.rank.ctypes.data,
+                         scale=self.scale.ctypes.data, r_max=r_max)
+        self.routing = Routing(n_tokens=n_tokens, n_segments=self.seg_adapter.size,
+                               seg_offsets=self.seg_offsets.ctypes.data,
+                               seg_adapter=self.seg_adapter.ctypes.data,
+                               token_adapter=self.token_adapter.ctypes.data, policy=policy)
+
+    def set_policy(self, policy: int):
+        self.routing.policy = policy
+
+
+def workspace_size(call: Call) -> int:
+    n = _c_i64()
+    _check(load().slora_workspace_size(ctypes.byref(call.lora), ctypes.byref(call.routing),
+                                       ctypes.byref(n)), "workspace_size")
+    return n.value
+
+
+def shrink(call: Call, x: int, v: int, ws: int, ws_bytes: int, stream: int):
+    _check(load().slora_shrink(ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(x), _vp(v),
+                               _vp(ws), ws_bytes, _vp(stream)), "shrink")
+
+
+def expand(call: Call, v: int, y: int, ws: int, ws_bytes: int, stream: int):
+    _check(load().slora_expand(ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(v), _vp(y),
+                               _vp(ws), ws_bytes, _vp(stream)), "expand")
+
+
+def apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
+    _check(load().slora_apply(ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(x), _vp(y),
+                              _vp(ws), ws_bytes, _vp(stream)), "apply")
+
+
+def plan_inspect(call: Call):
+    """(groups [n x 5] int32: family, first slot, count, pt_base, rank; tokens int32)."""
+    lib = load()
+    n = _c_i32()
+    cap = max(call.routing.n_tokens, 1)
+    info = np.empty(5 * cap, np.int32)
+    toks = np.empty(cap, np.int32)
+    _check(lib.slora_plan_inspect(ctypes.byref(call.lora), ctypes.byref(call.routing),
+                                  ctypes.byref(n), _p(info), cap, _p(toks)), "plan_inspect")
+    g = info[:5 * n.value].reshape(n.value, 5)
+    used = int(g[:, 2].sum()) if n.value else 0
+    return g, toks[:used]

@@ -1,0 +1,151 @@
+"""Device-memory and stream plumbing around libslora for one workload instance.
+
+PyTorch only allocates device and pinned host memory and provides streams and
+events; every step of the LoRA path (allocation bookkeeping, fetch, planning,
+shrink, expand) runs in libslora. Used by the tests, the smoke check and the
+benchmark.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+
+SENTINEL_I16 = {"f16": 0x7E00, "bf16": 0x7FC0}  # quiet NaN bit patterns (both < 2^15)
+
+
+def _dev_i16(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device, non_blocking=False)
+
+
+class HostStore:
+    """Adapter weights of one projection set in one pinned host buffer (16-byte aligned rows)."""
+
+    def __init__(self, wl, adapters):
+        self.offsets: Dict[tuple, int] = {}
+        total = 0
+        for a in adapters:
+            r = int(wl.ranks[a])
+            for p, pr in enumerate(wl.projections):
+                for half, L in ((0, pr.d_in), (1, pr.d_out)):
+                    self.offsets[(a, p, half)] = total
+                    total += ((r * L * 2 + 255) // 256) * 256
+        self.buf = torch.empty(max(total, 256), dtype=torch.uint8, pin_memory=True)
+        host = self.buf.numpy()
+        for a in adapters:
+            for p in range(len(wl.projections)):
+                at, b = wl.adapter(int(a), p)
+                for half, arr in ((0, at), (1, b)):
+                    o = self.offsets[(a, p, half)]
+                    raw = np.ascontiguousarray(arr).view(np.uint8).ravel()
+                    host[o:o + raw.size] = raw
+        self.base_ptr = self.buf.data_ptr()
+
+    def ptrs(self, a, n_proj):
+        return ([self.base_ptr + self.offsets[(a, p, 0)] for p in range(n_proj)],
+                [self.base_ptr + self.offsets[(a, p, 1)] for p in range(n_proj)])
+
+
+class PagedLoRA:
+    """One workload on one GPU: pool, resident adapters, page tables, inputs, workspace."""
+
+    def __init__(self, wl, device: str = "cuda", adapters: Optional[List[int]] = None,
+                 fill_kv: bool = True, sentinel: bool = True, pool_seed: Optional[int] = None):
+        self.wl = wl
+        self.device = torch.device(device)
+        P = wl.page_elems
+        self.pool_t = torch.empty(wl.n_pages * P, dtype=torch.int16, device=self.device)
+        if sentinel:
+            self.pool_t.fill_(SENTINEL_I16[wl.dtype])
+        self.pool = _lib.Pool(self.pool_t.data_ptr(), wl.n_pages, P, wl.dtype,
+                              wl.pool_seed if pool_seed is None else pool_seed)
+        self.adapters = [int(a) for a in (wl.active_adapters() if adapters is None else adapters)]
+        d_in = [p.d_in for p in wl.projections]
+        d_out = [p.d_out for p in wl.projections]
+        for a in self.adapters:
+            self.pool.alloc_adapter(a, int(wl.ranks[a]), d_in, d_out)
+        self.kv_pages = np.zeros(0, np.int32)
+        if fill_kv:
+            self._fill_kv()
+        self.store = HostStore(wl, self.adapters)
+        self.fetch()
+        self.pt_dev, self.pt_len, self.base, self.rank = [], [], [], []
+        for p in range(len(wl.projections)):
+            pt, base, rank = self.pool.page_table(p, wl.n_adapters)
+            self.pt_len.append(int(pt.size))
+            self.pt_dev.append(torch.from_numpy(np.ascontiguousarray(pt)).to(self.device)
+                               if pt.size else torch.zeros(1, dtype=torch.int32, device=self.device))
+            self.base.append(base)
+            self.rank.append(rank)
+        self.r_max = int(max([int(wl.ranks[a]) for a in self.adapters] + [0]))
+        self.r_max = max(self.r_max, 1)
+
+    def _fill_kv(self):
+        free = self.pool.info()["n_free"]
+        lens = self.wl.kv_seq_lens
+        got = []
+        if lens.size:
+            for L in lens:  # one K and one V page per token, until the pool is full
+                n = int(min(2 * int(L), free))
+                if n <= 0:
+                    break
+                got.append(self.pool.alloc_kv(n))
+                free -= n
+        elif free > 0:
+            got.append(self.pool.alloc_kv(free))
+        self.kv_pages = np.concatenate(got) if got else np.zeros(0, np.int32)
+
+    def fetch(self, adapters: Optional[List[int]] = None):
+        """Fetch adapters on a side stream; the current stream waits for the done event."""
+        side = torch.cuda.Stream(device=self.device)
+        done = torch.cuda.Event()
+        done.record(side)  # creates the event so its handle can be passed down
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        n_proj = len(self.wl.projections)
+        todo = self.adapters if adapters is None else adapters
+        for i, a in enumerate(todo):
+            at, b = self.store.ptrs(a, n_proj)
+            last = i == len(todo) - 1
+            self.pool.fetch_async(a, at, b, side.cuda_stream, done.cuda_event if last else None)
+        torch.cuda.current_stream(self.device).wait_event(done)
+        self._fetch_done = done
+
+    def call(self, proj: int, policy: int = _lib.POLICY_AUTO, wl=None) -> _lib.Call:
+        wl = wl or self.wl
+        p = wl.projections[proj]
+        return _lib.Call(pool_ptr=self.pool_t.data_ptr(), n_pages=wl.n_pages,
+                         page_elems=wl.page_elems, dtype=wl.dtype, d_in=p.d_in, d_out=p.d_out,
+                         page_table_ptr=self.pt_dev[proj].data_ptr(),
+                         page_table_len=self.pt_len[proj], base=self.base[proj], rank=wl.ranks,
+                         scale=wl.scales.astype(np.float32), r_max=self.r_max,
+                         n_tokens=wl.n_tokens, seg_offsets=wl.seg_offsets,
+                         seg_adapter=wl.seg_adapter, token_adapter=wl.token_adapter,
+                         policy=policy)
+
+    def inputs(self, proj: int):
+        """(x, y) device tensors for a projection; y holds y0."""
+        return _dev_i16(self.wl.x(proj), self.device), _dev_i16(self.wl.y0(proj), self.device)
+
+    def workspace(self, call: _lib.Call) -> torch.Tensor:
+        return torch.empty(_lib.workspace_size(call), dtype=torch.uint8, device=self.device)
+
+    def apply(self, call: _lib.Call, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
+              stream: Optional[torch.cuda.Stream] = None):
+        s = stream or torch.cuda.current_stream(self.device)
+        _lib.apply(call, x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), s.cuda_stream)
+
+    def shrink(self, call, x, v, ws, stream=None):
+        s = stream or torch.cuda.current_stream(self.device)
+        _lib.shrink(call, x.data_ptr(), v.data_ptr(), ws.data_ptr(), ws.numel(), s.cuda_stream)
+
+    def expand(self, call, v, y, ws, stream=None):
+        s = stream or torch.cuda.current_stream(self.device)
+        _lib.expand(call, v.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), s.cuda_stream)
+
+    def close(self):
+        torch.cuda.synchronize(self.device)
+        self.pool.destroy()

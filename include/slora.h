@@ -1,0 +1,201 @@
+/*
+ * slora.h - C ABI of the heterogeneous batched LoRA library (libslora.so, gfx950).
+ *
+ * What the library computes. For every token t of a mixed batch, with i = a(t)
+ * the adapter that token uses, r_i its rank and s_i its scale:
+ *
+ *     v[t, k] = sum_j x[t, j] * A_i[j, k]                       (shrink, k < r_i)
+ *     y[t, n] = y0[t, n] + s_i * sum_k v[t, k] * B_i[k, n]       (expand)
+ *
+ * y[t, :] = y0[t, :] bit for bit when t has no adapter (id -1) or r_i = 0.
+ * Sources: "Makale Bulteni - S-LoRA", section "Iddia ve Gerceklik: S-LoRA" (one
+ * batched GEMM needs one weight; the S-LoRA kernel multiplies every token of a
+ * batch by its own adapter; ranks such as 8, 16, 64 coexist); the paper review
+ * "S-LoRA: Serving Thousands of Concurrent LoRA Adapters", abstract and section
+ * "Proposed method" (all adapters live in host memory, the active ones are
+ * fetched to GPU memory on demand; base-model compute is separate, so y0 is an
+ * input); the S-LoRA overview (Chinese), sections "1. Unified Paging" and
+ * "2. Heterogeneous Batching" (one memory pool for adapter weights of any rank
+ * and for KV-cache tensors; kernels that read non-contiguous memory directly).
+ *
+ * Memory model. Every device buffer (pool, page table, x, y, v, workspace) is
+ * allocated and owned by the caller. The library owns host bookkeeping (the pool
+ * handle) and a small pinned staging ring for work lists. All compute calls are
+ * asynchronous on the stream they are given; argument validation is synchronous.
+ *
+ * Paged layout. The pool is n_pages pages of page_elems elements of one dtype.
+ * A page holds one chunk of one row: adapter i's projection p occupies, for each
+ * of its r rows of A^T (row k = column k of A, length d_in) ceil(d_in/P) pages,
+ * then for each of its r rows of B (length d_out) ceil(d_out/P) pages. The last
+ * chunk of a row whose length is not a multiple of P leaves the page tail unused.
+ * KV-cache pages come from the same free list and are never read by this library.
+ * Page tables are int32 arrays; adapter i's entries start at base[i] in that
+ * order (A^T rows, chunks ascending; then B rows, chunks ascending).
+ *
+ * Errors. Every call returns SLORA_OK (0) or a negative code; slora_last_error()
+ * returns a thread-local message for the last failure on the calling thread.
+ * A failing call changes nothing (allocation is all-or-nothing).
+ *
+ * Threads. A pool handle is not thread-safe: one owner at a time. Compute calls
+ * may run from several threads on different streams.
+ */
+#ifndef SLORA_H_
+#define SLORA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLORA_ABI_VERSION 1
+
+#define SLORA_OK 0
+#define SLORA_E_INVALID (-1)   /* bad argument, shape, alignment or routing */
+#define SLORA_E_POOL_FULL (-2) /* not enough free pages; nothing was allocated */
+#define SLORA_E_STATE (-3)     /* adapter absent / already resident / fetch in flight */
+#define SLORA_E_HIP (-4)       /* a HIP runtime call failed */
+
+#define SLORA_F16 0  /* IEEE binary16 */
+#define SLORA_BF16 1 /* bfloat16 */
+
+/* Which kernel family serves which tokens (slora_routing.policy). */
+#define SLORA_POLICY_AUTO 0  /* segment tokens -> SGMV (MFMA), per-token ids -> MBGMV */
+#define SLORA_POLICY_MBGMV 1 /* every routed token -> MBGMV (segments grouped like ids) */
+#define SLORA_POLICY_SGMV 2  /* every routed token -> SGMV (ids bucketed by adapter) */
+
+typedef struct slora_pool slora_pool; /* opaque host-side handle */
+
+/* Message for the last failing call on this thread ("" if none). Never NULL. */
+const char* slora_last_error(void);
+
+/* SLORA_ABI_VERSION of the loaded library. */
+int slora_abi_version(void);
+
+/* ------------------------------------------------------------------ unified pool
+ * Unified Paging (S-LoRA overview, section "1. Unified Paging"; review, section
+ * "Proposed method"): one pool of fixed-size pages shared by adapter weights of
+ * any rank and by KV-cache pages, allocated from one free list. The free list is
+ * shuffled with shuffle_seed, so allocations land on scattered pages, the way
+ * pages of a long-running server end up.
+ */
+
+/* Create a pool over caller-owned device memory dev_pages (n_pages * page_elems
+ * elements of dtype, 16-byte aligned). page_elems must be a positive multiple of
+ * 8. The pool never frees dev_pages. Returns the handle in *out. */
+int slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
+                      uint64_t shuffle_seed, slora_pool** out);
+
+/* Destroy the handle (waits for this pool's fetches to finish). NULL is a no-op. */
+int slora_pool_destroy(slora_pool* pool);
+
+/* Pool geometry and the number of free pages. Any output pointer may be NULL. */
+int slora_pool_info(const slora_pool* pool, int64_t* n_pages, int64_t* n_free,
+                    int32_t* page_elems, int32_t* dtype);
+
+/* Take n pages for KV cache from the shared free list; their ids go to
+ * out_page_ids[n]. SLORA_E_POOL_FULL (nothing taken) if fewer than n are free. */
+int slora_pool_alloc_kv(slora_pool* pool, int32_t n, int32_t* out_page_ids);
+
+/* Return KV pages to the free list. Every id must be a KV page of this pool. */
+int slora_pool_free_kv(slora_pool* pool, const int32_t* page_ids, int32_t n);
+
+/* Reserve pages for adapter `adapter_id` (>= 0): rank r >= 0 (shared by its
+ * projections) and n_proj projections with shapes d_in[p] x d_out[p] (multiples
+ * of 8). All-or-nothing: SLORA_E_POOL_FULL when the free list is too short,
+ * SLORA_E_STATE when the adapter is already resident. */
+int slora_pool_alloc_adapter(slora_pool* pool, int32_t adapter_id, int32_t rank, int32_t n_proj,
+                             const int32_t* d_in, const int32_t* d_out);
+
+/* Return the adapter's pages. SLORA_E_STATE if it is not resident or if a fetch
+ * into it has not finished yet (checked with hipEventQuery, never waits). */
+int slora_pool_free_adapter(slora_pool* pool, int32_t adapter_id);
+
+/* Export projection `proj`'s page table for adapters 0..n_adapters-1 into the host
+ * array pt[pt_cap]: resident adapters' entries in ascending id order, in the
+ * layout described above. base[i] gets the first entry (-1 when adapter i is not
+ * resident or has no projection `proj`), rank[i] its rank (0 when absent).
+ * *pt_len gets the number of entries written (pt may be NULL with pt_cap 0 to
+ * query the length). The caller copies pt to device memory for the compute calls. */
+int slora_pool_page_table(const slora_pool* pool, int32_t proj, int32_t n_adapters, int32_t* pt,
+                          int64_t pt_cap, int64_t* pt_len, int64_t* base, int32_t* rank);
+
+/* Owner of every page, for inspection: owner[p] = adapter id, -1 free, -2 KV. */
+int slora_pool_owners(const slora_pool* pool, int32_t* owner);
+
+/* Copy a resident adapter's weights from host memory into its pages, page by
+ * page, asynchronously on side_stream (a hipStream_t), then record done_event (a
+ * hipEvent_t, may be NULL) on it. Review, abstract and "Proposed method"; "Makale
+ * Bulteni - S-LoRA", section "Iddia ve Gerceklik" (DRAM -> GPU, page by page,
+ * asynchronously).
+ *   host_AT[p]: pinned host memory (hipHostMalloc / torch pin_memory), r x d_in[p]
+ *               row-major, row k = column k of A.
+ *   host_B[p] : pinned host memory, r x d_out[p] row-major.
+ * The host buffers must stay alive and unchanged until done_event completes. The
+ * compute stream must wait for done_event (hipStreamWaitEvent) before a compute
+ * call reads the adapter. Pages of other adapters and KV pages are never written. */
+int slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
+                      const void* const* host_B, void* side_stream, void* done_event);
+
+/* ------------------------------------------------------------------ compute */
+
+/* One projection of the batch. All pointers are read only. */
+typedef struct {
+  const void* pool;          /* DEVICE: the pool's pages (as given to slora_pool_create) */
+  int64_t n_pages;           /* pool size in pages; page ids >= n_pages read as NaN */
+  int32_t page_elems;        /* P */
+  int32_t dtype;             /* SLORA_F16 | SLORA_BF16 (x, y and pool) */
+  int32_t d_in, d_out;       /* multiples of 8 */
+  const int32_t* page_table; /* DEVICE int32 [page_table_len] */
+  int64_t page_table_len;
+  int32_t n_adapters;
+  const int64_t* base;       /* HOST [n_adapters]: first page-table entry, -1 = not resident */
+  const int32_t* rank;       /* HOST [n_adapters]: 0 allowed (delta is zero) */
+  const float* scale;        /* HOST [n_adapters]: s_i (alpha / r_i in the standard form) */
+  int32_t r_max;             /* row stride of v; >= every rank a routed token uses, <= 128 */
+} slora_lora;
+
+/* Which adapter each token uses (all HOST arrays). Tokens [0, seg_offsets[S])
+ * are routed by segments (a request's contiguous tokens share one adapter);
+ * tokens [seg_offsets[S], n_tokens) by one id each. Ids are in [-1, n_adapters). */
+typedef struct {
+  int32_t n_tokens;
+  int32_t n_segments;           /* S >= 0 */
+  const int32_t* seg_offsets;   /* [S + 1], seg_offsets[0] = 0, nondecreasing; NULL if S = 0 */
+  const int32_t* seg_adapter;   /* [S] */
+  const int32_t* token_adapter; /* [n_tokens - seg_offsets[S]], -1 = no adapter */
+  int32_t policy;               /* SLORA_POLICY_* */
+} slora_routing;
+
+/* Device workspace bytes a compute call with these arguments needs (>= 256). */
+int slora_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes);
+
+/* Shrink only: v[t, k] (fp32, DEVICE [n_tokens x r_max]) for routed tokens and
+ * k < rank; other entries of v are left unchanged. x: DEVICE [n_tokens x d_in]. */
+int slora_shrink(const slora_lora* lora, const slora_routing* routing, const void* x, float* v,
+                 void* ws, int64_t ws_bytes, void* stream);
+
+/* Expand only, in place: y (DEVICE [n_tokens x d_out], holds y0 on entry) gets
+ * y0 + s * v B for routed tokens, rounded once (round to nearest even) from
+ * fp32. Rows of unrouted tokens are not touched. */
+int slora_expand(const slora_lora* lora, const slora_routing* routing, const float* v, void* y,
+                 void* ws, int64_t ws_bytes, void* stream);
+
+/* Shrink + expand in one call (v lives in the workspace). y holds y0 on entry. */
+int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
+                void* ws, int64_t ws_bytes, void* stream);
+
+/* Work lists a call with these arguments would run, for inspection and tests
+ * (host only; validates exactly like slora_apply, launches nothing). Groups come
+ * in dispatch order; for group g, info[5g .. 5g+4] = {family (0 MBGMV, 1 SGMV),
+ * first slot in tokens[], token count, first page-table entry, rank}. tokens gets
+ * the routed token ids grouped (n_tokens entries suffice). *n_groups gets the
+ * group count; SLORA_E_INVALID if it exceeds info_cap. */
+int slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int32_t* n_groups,
+                       int32_t* info, int32_t info_cap, int32_t* tokens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLORA_H_ */

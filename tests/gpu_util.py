@@ -1,0 +1,74 @@
+"""Helpers for the GPU tests: run the HIP path through libslora, compare with the oracle."""
+
+import sys
+
+import numpy as np
+
+import oracle
+import workloads
+
+TOL = 5e-3  # max|y - y_ref| <= TOL * max(1, ||y_ref||_inf), fp16/bf16 in, fp32 accumulation
+
+
+def decode(bits, dtype):
+    bits = np.asarray(bits).view(np.uint16)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def check_close(y_gpu_bits, y_ref, dtype, what=""):
+    y = decode(y_gpu_bits, dtype)
+    assert y.shape == y_ref.shape, (y.shape, y_ref.shape)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite GPU output at {np.argwhere(~np.isfinite(y))[:5]}"
+    scale = max(1.0, float(np.max(np.abs(y_ref))))
+    err = float(np.max(np.abs(y - y_ref)))
+    assert err <= TOL * scale, f"{what}: max err {err:.3e} > {TOL} * {scale:.3f}"
+    return err / scale
+
+
+def sample_tokens(wl, n, seed=0):
+    """Evaluation rows: ends of every segment (ragged tails), both ends of the batch, random rest."""
+    T = wl.n_tokens
+    rng = np.random.default_rng(seed)
+    pick = {0, T - 1}
+    so = wl.seg_offsets
+    for s in range(len(wl.seg_adapter)):
+        if so[s + 1] > so[s]:
+            pick.update([int(so[s]), int(so[s + 1]) - 1])
+    pick.update(int(t) for t in rng.choice(T, size=min(n, T), replace=False))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+class CodedWorkload(workloads.Workload):
+    """Adapter weights replaced by exact small-integer codes (probe tests).
+
+    Element j of A^T row k of adapter a, projection p, is code(a, p, k, j); B rows
+    use a second code. |codes| <= 120, exact in fp16 and bf16.
+    """
+
+    @staticmethod
+    def code(a, p, k, j, half):
+        return ((a * 37 + p * 11 + k * 7 + j * 3 + half * 5) % 241) - 120
+
+    def adapter(self, adapter_id, proj):
+        p = self.projections[proj]
+        r = int(self.ranks[adapter_id])
+        k = np.arange(r)[:, None]
+        at = self.code(adapter_id, proj, k, np.arange(p.d_in)[None, :], 0).astype(np.float32)
+        b = self.code(adapter_id, proj, k, np.arange(p.d_out)[None, :], 1).astype(np.float32)
+        return workloads.to_bits(at, self.dtype), workloads.to_bits(b, self.dtype)
+
+
+def coded(wl):
+    c = CodedWorkload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__ if f != "_cache"})
+    return c
+
+
+def oracle_ref(wl, proj, eval_tokens=None, want_v=False, x=None, y0=None, n_threads=8):
+    return oracle.reference(wl, proj, eval_tokens, want_v=want_v, x=x, y0=y0, n_threads=n_threads)

@@ -1,0 +1,287 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Each case names itself on stderr before it touches the GPU. The oracle builds
+its own pool and page table; nothing it consumes comes from the GPU path.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import (TOL, CodedWorkload, check_close, coded, oracle_ref, sample_tokens, say)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from heterogeneous_lora_amd import _lib, runtime
+    _lib.load()
+    return runtime
+
+
+def _run(rt, wl, proj=0, policy=0, mode="apply", inst=None, x=None, y0=None):
+    from heterogeneous_lora_amd import _lib
+    inst = inst or rt.PagedLoRA(wl)
+    call = inst.call(proj, policy)
+    xd, yd = inst.inputs(proj)
+    if x is not None:
+        xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    if y0 is not None:
+        yd = torch.from_numpy(np.ascontiguousarray(y0).view(np.int16)).cuda()
+    ws = inst.workspace(call)
+    if mode == "apply":
+        inst.apply(call, xd, yd, ws)
+        torch.cuda.synchronize()
+        return yd.cpu().numpy().view(np.uint16), inst
+    v = torch.zeros(wl.n_tokens, inst.r_max, dtype=torch.float32, device="cuda")
+    inst.shrink(call, xd, v, ws)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), inst
+
+
+SMALL = [
+    dict(seed=101),
+    dict(seed=102, dtype="bf16"),
+    dict(seed=103, d_in=1000, d_out=520, page_elems=64, n_tokens=70, n_segments=5,
+         rank_choices=(0, 1, 3, 8, 16, 40)),
+    dict(seed=104, dtype="bf16", d_in=520, d_out=1032, page_elems=512, n_tokens=41,
+         n_segments=0, rank_choices=(8, 64, 128), n_adapters=4),
+    dict(seed=105, d_in=4096, d_out=1024, page_elems=1024, n_tokens=37, n_segments=2,
+         rank_choices=(5, 16, 33), n_adapters=6),
+    dict(seed=106, dtype="bf16", d_in=2048, d_out=4104, page_elems=2048, n_tokens=33,
+         n_segments=0, rank_choices=(16, 24), n_adapters=3),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=[f"s{k['seed']}" for k in SMALL])
+@pytest.mark.parametrize("policy", [1], ids=["mbgmv"])
+def test_small_parity(rt, kw, policy):
+    wl = workloads.random_small(**kw)
+    say(f"[gpu] small parity {kw} policy={policy}")
+    y, inst = _run(rt, wl, policy=policy)
+    ref, _ = oracle_ref(wl, 0)
+    check_close(y, ref, wl.dtype, f"small {kw}")
+    inst.close()
+
+
+def test_tiny_decode_parity(rt):
+    wl = workloads.tiny(0)
+    say("[gpu] tiny_decode parity")
+    y, inst = _run(rt, wl)
+    ref, _ = oracle_ref(wl, 0)
+    check_close(y, ref, wl.dtype, "tiny_decode")
+    inst.close()
+
+
+@pytest.fixture(scope="module")
+def decode7b(rt):
+    wl = workloads.decode7b(0)
+    say("[gpu] building decode_7b instance")
+    inst = rt.PagedLoRA(wl)
+    yield wl, inst
+    inst.close()
+
+
+def test_decode7b_parity(rt, decode7b):
+    wl, inst = decode7b
+    say("[gpu] decode_7b parity (all 256 tokens)")
+    y, _ = _run(rt, wl, inst=inst)
+    ref, _ = oracle_ref(wl, 0)
+    rel = check_close(y, ref, wl.dtype, "decode_7b")
+    say(f"[gpu] decode_7b max err / scale = {rel:.2e} (tol {TOL})")
+
+
+def test_decode7b_shrink_v(rt, decode7b):
+    wl, inst = decode7b
+    say("[gpu] decode_7b shrink v parity")
+    v, _ = _run(rt, wl, inst=inst, mode="shrink")
+    _, v_ref = oracle_ref(wl, 0, want_v=True)
+    ids = wl.token_adapter
+    for t in range(wl.n_tokens):
+        r = int(wl.ranks[ids[t]])
+        scale = max(1.0, float(np.max(np.abs(v_ref[t, :r]))))
+        err = float(np.max(np.abs(v[t, :r] - v_ref[t, :r])))
+        assert err <= TOL * scale, (t, err, scale)
+
+
+def test_decode7b_expand_only(rt, decode7b):
+    """slora_expand fed the oracle's v (as fp32) reproduces the oracle's y."""
+    wl, inst = decode7b
+    say("[gpu] decode_7b expand-only parity")
+    ref, v_ref = oracle_ref(wl, 0, want_v=True)
+    call = inst.call(0)
+    _, yd = inst.inputs(0)
+    vt = torch.zeros(wl.n_tokens, inst.r_max, dtype=torch.float32)
+    vt[:, :v_ref.shape[1]] = torch.from_numpy(v_ref.astype(np.float32))
+    vt = vt.cuda()
+    ws = inst.workspace(call)
+    inst.expand(call, vt, yd, ws)
+    torch.cuda.synchronize()
+    check_close(yd.cpu().numpy().view(np.uint16), ref, wl.dtype, "decode_7b expand")
+
+
+def test_decode7b_batch_invariance(rt, decode7b):
+    """A token's output does not depend on which other tokens share its batch (bit-exact)."""
+    wl, inst = decode7b
+    say("[gpu] decode_7b batch invariance")
+    y_all, _ = _run(rt, wl, inst=inst)
+    sub = workloads.decode7b(0)
+    keep = np.arange(0, wl.n_tokens, 3)
+    sub.token_adapter = wl.token_adapter[keep].copy()
+    x = wl.x(0)[keep]
+    y0 = wl.y0(0)[keep]
+    call = inst.call(0, wl=sub)
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    yd = torch.from_numpy(np.ascontiguousarray(y0).view(np.int16)).cuda()
+    ws = inst.workspace(call)
+    inst.apply(call, xd, yd, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(yd.cpu().numpy().view(np.uint16), y_all[keep])
+
+
+def test_page_permutation_bit_identical(rt):
+    """Two pools with different shuffles (so every page sits elsewhere) give identical bits."""
+    wl = workloads.random_small(201, d_in=1024, d_out=1536, page_elems=512, n_tokens=40,
+                                n_segments=0, rank_choices=(8, 16, 32), n_pages=4096)
+    say("[gpu] page permutation")
+    a = rt.PagedLoRA(wl, pool_seed=1)
+    b = rt.PagedLoRA(wl, pool_seed=2)
+    assert not np.array_equal(a.pt_dev[0].cpu().numpy(), b.pt_dev[0].cpu().numpy())
+    ya, _ = _run(rt, wl, inst=a)
+    yb, _ = _run(rt, wl, inst=b)
+    assert np.array_equal(ya, yb)
+    a.close()
+    b.close()
+
+
+def test_idle_tokens_untouched(rt):
+    wl = workloads.random_small(202, n_tokens=60, n_segments=0, p_none=0.4,
+                                rank_choices=(0, 0, 8, 16), d_in=512, d_out=768, page_elems=256)
+    say("[gpu] idle tokens pass through")
+    y, inst = _run(rt, wl, policy=1)
+    ids = wl.token_adapter
+    idle = (ids < 0) | (wl.ranks[np.maximum(ids, 0)] == 0)
+    assert idle.any() and (~idle).any()
+    assert np.array_equal(y[idle], wl.y0(0)[idle])
+    inst.close()
+
+
+def test_fetch_byte_exact_and_sentinels(rt):
+    """Pages hold exactly the host rows; page tails, KV and free pages keep the NaN sentinel."""
+    wl = workloads.random_small(203, d_in=1000, d_out=264, page_elems=256, n_tokens=30,
+                                n_segments=0, rank_choices=(3, 8), n_adapters=4, n_pages=300)
+    say("[gpu] fetch byte-exact")
+    inst = rt.PagedLoRA(wl)
+    torch.cuda.synchronize()
+    pool = inst.pool_t.cpu().numpy().view(np.uint16).reshape(wl.n_pages, wl.page_elems)
+    P = wl.page_elems
+    p = wl.projections[0]
+    cA, cB = -(-p.d_in // P), -(-p.d_out // P)
+    pt = inst.pt_dev[0].cpu().numpy()
+    sentinel = rt.SENTINEL_I16[wl.dtype]
+    touched = np.zeros(wl.n_pages, bool)
+    for a in inst.adapters:
+        at, b = wl.adapter(a, 0)
+        r = at.shape[0]
+        base = int(inst.base[0][a])
+        for k in range(r):
+            for half, rows, c, L in ((0, at, cA, p.d_in), (1, b, cB, p.d_out)):
+                for ch in range(c):
+                    e = base + (0 if half == 0 else r * cA) + k * c + ch
+                    page = pt[e]
+                    n = min(P, L - ch * P)
+                    assert np.array_equal(pool[page, :n], rows[k, ch * P:ch * P + n]), (a, k, half, ch)
+                    assert np.all(pool[page, n:] == sentinel)
+                    touched[page] = True
+    assert np.all(pool[~touched] == sentinel)
+    owners = inst.pool.owners()
+    assert set(np.nonzero(touched)[0]) == set(np.nonzero(owners >= 0)[0])
+    inst.close()
+
+
+def test_probe_codes_bit_exact(rt):
+    """Integer-coded adapters: one-hot x reads back A^T codes exactly through shrink; one-hot
+    A^T rows route v = e_m to B row m exactly through apply (gathers and routing bit-exact)."""
+    for dt in ("f16", "bf16"):
+        base_wl = workloads.random_small(204, dtype=dt, d_in=1536, d_out=1040, page_elems=512,
+                                         n_tokens=24, n_segments=0, rank_choices=(4, 8, 16),
+                                         p_none=0.0, n_adapters=5)
+        wl = coded(base_wl)
+        say(f"[gpu] probe codes {dt}")
+        inst = rt.PagedLoRA(wl)
+        p = wl.projections[0]
+        js = np.random.default_rng(5).choice(p.d_in, size=wl.n_tokens)
+        x = np.zeros((wl.n_tokens, p.d_in), np.float32)
+        x[np.arange(wl.n_tokens), js] = 1.0
+        xb = workloads.to_bits(x, dt)
+        call = inst.call(0, 1)
+        v = torch.zeros(wl.n_tokens, inst.r_max, dtype=torch.float32, device="cuda")
+        ws = inst.workspace(call)
+        inst.shrink(call, torch.from_numpy(xb.view(np.int16)).cuda(), v, ws)
+        torch.cuda.synchronize()
+        v = v.cpu().numpy()
+        for t in range(wl.n_tokens):
+            a = int(wl.token_adapter[t])
+            r = int(wl.ranks[a])
+            want = _codes(a, r, js[t])
+            assert np.array_equal(v[t, :r], want), (dt, t)
+        inst.close()
+
+
+def _codes(a, r, j):
+    return np.array([CodedWorkload.code(a, 0, k, j, 0) for k in range(r)], np.float32)
+
+
+def test_fetch_waits_and_free_state(rt):
+    """A fetch queued behind a slow side stream is still complete when apply runs after the
+    event; freeing the adapter while that fetch is in flight is refused (E_STATE)."""
+    from heterogeneous_lora_amd import _lib
+    wl = workloads.random_small(205, d_in=512, d_out=512, page_elems=512, n_tokens=16,
+                                n_segments=0, rank_choices=(8,), p_none=0.0, n_adapters=2)
+    say("[gpu] fetch ordering / E_STATE")
+    inst = rt.PagedLoRA(wl)
+    torch.cuda.synchronize()
+    inst.pool_t.fill_(rt.SENTINEL_I16[wl.dtype])  # wipe fetched pages
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    done.record(side)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(50_000_000)  # bounded spin delays the side stream
+    side.wait_stream(torch.cuda.current_stream())
+    for a in inst.adapters:
+        at, b = inst.store.ptrs(a, 1)
+        inst.pool.fetch_async(a, at, b, side.cuda_stream, done.cuda_event)
+    with pytest.raises(_lib.SloraError) as e:
+        inst.pool.free_adapter(inst.adapters[0])
+    assert e.value.code == _lib.E_STATE
+    torch.cuda.current_stream().wait_event(done)
+    y, _ = _run(rt, wl, inst=inst, policy=1)
+    ref, _ = oracle_ref(wl, 0)
+    check_close(y, ref, wl.dtype, "fetch ordering")
+    torch.cuda.synchronize()
+    inst.pool.free_adapter(inst.adapters[0])
+    inst.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["mixed_13b", "mlp_asym"])
+def test_large_mbgmv_sampled(rt, name):
+    """Full-size workloads through MBGMV for every token, checked on sampled rows."""
+    wl = workloads.make(name)
+    say(f"[gpu] {name} (MBGMV for all tokens), building instance")
+    inst = rt.PagedLoRA(wl)
+    ev = sample_tokens(wl, 48)
+    for proj in range(len(wl.projections)):
+        say(f"[gpu] {name} proj {wl.projections[proj].name}")
+        y, _ = _run(rt, wl, proj=proj, policy=1, inst=inst)
+        ref, _ = oracle_ref(wl, proj, ev)
+        check_close(y[ev], ref, wl.dtype, f"{name}/{proj}")
+        ids = np.concatenate([np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets)), wl.token_adapter])
+        idle = ids < 0
+        if idle.any():
+            assert np.array_equal(y[idle], wl.y0(proj)[idle])
+    inst.close()

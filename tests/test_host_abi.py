@@ -1,0 +1,259 @@
+"""Host-side tests of libslora (CPU only: no HIP call reaches a device here).
+
+* every function include/slora.h declares is exported;
+* the unified pool's allocator: disjoint owners, page accounting, seeded
+  determinism, all-or-nothing failure, state errors, page-table export layout;
+* argument / routing validation of the compute calls (rejected before any launch);
+* the planner's work lists, compared entry by entry with an independent Python
+  model of the grouping rules.
+"""
+
+import re
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+from heterogeneous_lora_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_DEV = 0x7F0000000000  # never dereferenced by host code
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_symbols_exported(lib):
+    hdr = open(os.path.join(ROOT, "include", "slora.h")).read()
+    names = set(re.findall(r"^\s*(?:int|const char\*)\s+(slora_\w+)\s*\(", hdr, re.M))
+    assert len(names) >= 17
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert _lib.abi_version() == 1
+
+
+def _pool(n_pages=512, P=64, seed=3, dtype="f16"):
+    return _lib.Pool(FAKE_DEV, n_pages, P, dtype, seed)
+
+
+def test_pool_accounting_and_ownership():
+    pool = _pool()
+    pool.alloc_adapter(0, 8, [128, 64], [64, 200])   # cA = 2,1; cB = 1,4
+    pool.alloc_adapter(5, 4, [128, 64], [64, 200])
+    pool.alloc_adapter(2, 0, [128, 64], [64, 200])   # rank 0: no pages
+    kv = pool.alloc_kv(37)
+    own = pool.owners()
+    need0 = 8 * ((2 + 1) + (1 + 4))
+    need5 = 4 * ((2 + 1) + (1 + 4))
+    assert (own == 0).sum() == need0 and (own == 5).sum() == need5
+    assert (own == -2).sum() == 37 and set(own[kv]) == {-2}
+    assert pool.info()["n_free"] == 512 - need0 - need5 - 37 == (own == -1).sum()
+    for proj, (cA, cB) in enumerate([(2, 1), (1, 4)]):
+        pt, base, rank = pool.page_table(proj, 8)
+        assert list(rank) == [8, 0, 0, 0, 0, 4, 0, 0]
+        assert base[0] == 0 and base[2] == 8 * (cA + cB) and base[5] == base[2]
+        assert base[1] == base[3] == base[4] == base[6] == base[7] == -1
+        assert pt.size == 12 * (cA + cB)
+        assert set(own[pt[:base[5]]]) == {0} and set(own[pt[base[5]:]]) == {5}
+    # the two projections' pages are disjoint and together are all the adapter's pages
+    pt0, b0, _ = pool.page_table(0, 8)
+    pt1, b1, _ = pool.page_table(1, 8)
+    assert set(pt0[:24]).isdisjoint(pt1[:40])
+    assert set(pt0[:24]) | set(pt1[:40]) == set(np.nonzero(own == 0)[0])
+    pool.free_kv(kv[:10])
+    assert pool.info()["n_free"] == 512 - need0 - need5 - 27
+    pool.free_adapter(0)
+    assert (pool.owners() == 0).sum() == 0
+    assert pool.info()["n_free"] == 512 - need5 - 27
+    pool.destroy()
+
+
+def test_pool_seeded_and_scattered():
+    a, b, c = _pool(seed=11), _pool(seed=11), _pool(seed=12)
+    for p in (a, b, c):
+        p.alloc_adapter(1, 16, [64], [64])
+    pa, pb, pc = (p.page_table(0, 2)[0] for p in (a, b, c))
+    assert np.array_equal(pa, pb) and not np.array_equal(pa, pc)
+    assert not np.array_equal(np.sort(pa), np.arange(pa.min(), pa.min() + pa.size))  # scattered
+    for p in (a, b, c):
+        p.destroy()
+
+
+def test_pool_errors_all_or_nothing():
+    pool = _pool(n_pages=40, P=64)
+    with pytest.raises(_lib.SloraError) as e:
+        pool.alloc_adapter(0, 32, [64], [64])  # 64 pages > 40
+    assert e.value.code == _lib.E_POOL_FULL
+    assert pool.info()["n_free"] == 40 and (pool.owners() == -1).all()
+    pool.alloc_adapter(0, 4, [64], [64])
+    with pytest.raises(_lib.SloraError) as e:
+        pool.alloc_adapter(0, 4, [64], [64])
+    assert e.value.code == _lib.E_STATE
+    with pytest.raises(_lib.SloraError) as e:
+        pool.alloc_kv(33)
+    assert e.value.code == _lib.E_POOL_FULL and pool.info()["n_free"] == 32
+    with pytest.raises(_lib.SloraError) as e:
+        pool.free_adapter(3)
+    assert e.value.code == _lib.E_STATE
+    own = pool.owners()
+    adapter_page = int(np.nonzero(own == 0)[0][0])
+    with pytest.raises(_lib.SloraError) as e:
+        pool.free_kv(np.array([adapter_page]))
+    assert e.value.code == _lib.E_INVALID
+    kv = pool.alloc_kv(2)
+    with pytest.raises(_lib.SloraError):
+        pool.free_kv(np.array([kv[0], kv[0]]))
+    assert (pool.owners()[kv] == -2).all()
+    for bad in (dict(d_in=[60], d_out=[64]), dict(d_in=[64], d_out=[64], rank=129),
+                dict(d_in=[64], d_out=[64], rank=-1)):
+        with pytest.raises(_lib.SloraError) as e:
+            pool.alloc_adapter(9, bad.get("rank", 4), bad["d_in"], bad["d_out"])
+        assert e.value.code == _lib.E_INVALID
+    pool.destroy()
+    with pytest.raises(_lib.SloraError):
+        _lib.Pool(FAKE_DEV + 8, 10, 64, "f16", 0)  # misaligned
+    with pytest.raises(_lib.SloraError):
+        _lib.Pool(FAKE_DEV, 10, 60, "f16", 0)  # P % 8 != 0
+
+
+# ------------------------------------------------------------------ compute-call validation
+
+def _call(wl, policy=_lib.POLICY_AUTO, pool=None, **over):
+    pool = pool or _lib.Pool(FAKE_DEV, wl.n_pages, wl.page_elems, wl.dtype, 1)
+    p = wl.projections[0]
+    for a in wl.active_adapters():
+        if a not in getattr(pool, "_resident", set()):
+            pool.alloc_adapter(int(a), int(wl.ranks[a]), [p.d_in], [p.d_out])
+    pool._resident = set(int(a) for a in wl.active_adapters())
+    pt, base, rank = pool.page_table(0, wl.n_adapters)
+    args = dict(pool_ptr=FAKE_DEV, n_pages=wl.n_pages, page_elems=wl.page_elems, dtype=wl.dtype,
+                d_in=p.d_in, d_out=p.d_out, page_table_ptr=FAKE_DEV, page_table_len=pt.size,
+                base=base, rank=wl.ranks, scale=wl.scales, r_max=max(int(wl.ranks.max()), 1),
+                n_tokens=wl.n_tokens, seg_offsets=wl.seg_offsets, seg_adapter=wl.seg_adapter,
+                token_adapter=wl.token_adapter, policy=policy)
+    args.update(over)
+    return _lib.Call(**args), pool, pt, base
+
+
+def _apply_code(call, ws_bytes=1 << 30):
+    try:
+        _lib.apply(call, FAKE_DEV, FAKE_DEV, FAKE_DEV, ws_bytes, 0)
+    except _lib.SloraError as e:
+        return e.code
+    return 0
+
+
+def test_validation_rejects_bad_calls():
+    wl = workloads.random_small(3, n_tokens=20, n_segments=3, rank_choices=(4, 8))
+    call, pool, pt, base = _call(wl)
+    used = [a for a in wl.active_adapters()]
+    cases = {
+        "id_out_of_range": (dict(token_adapter=np.full_like(wl.token_adapter, wl.n_adapters)), _lib.E_INVALID),
+        "id_below_minus_one": (dict(token_adapter=np.full_like(wl.token_adapter, -2)), _lib.E_INVALID),
+        "offsets_decrease": (dict(seg_offsets=np.array([0, 5, 2, 4], np.int32)), _lib.E_INVALID),
+        "offsets_past_end": (dict(seg_offsets=np.array([0, 5, 9, 21], np.int32),
+                                  token_adapter=np.zeros(0, np.int32)), _lib.E_INVALID),
+        "not_resident": (dict(base=np.full_like(base, -1)), _lib.E_STATE),
+        "rank_above_r_max": (dict(r_max=1), _lib.E_INVALID),
+        "r_max_too_big": (dict(r_max=129), _lib.E_INVALID),
+        "page_table_short": (dict(page_table_len=int(pt.size) - 1), _lib.E_INVALID),
+        "d_in_not_multiple_of_8": (dict(d_in=wl.projections[0].d_in + 4), _lib.E_INVALID),
+        "bad_policy": (dict(policy=7), _lib.E_INVALID),
+    }
+    assert len(wl.token_adapter) > 0 and used
+    for name, (over, code) in cases.items():
+        c, _, _, _ = _call(wl, pool=pool, **over)
+        assert _apply_code(c) == code, name
+    # workspace too small is rejected before anything is launched
+    c, _, _, _ = _call(wl, pool=pool)
+    assert _apply_code(c, ws_bytes=16) == _lib.E_INVALID
+    assert "workspace" in _lib.last_error()
+    # an all-idle batch (every id -1) does nothing and succeeds without touching HIP
+    c, _, _, _ = _call(wl, pool=pool, seg_adapter=np.full_like(wl.seg_adapter, -1),
+                       token_adapter=np.full_like(wl.token_adapter, -1))
+    assert _apply_code(c) == 0
+    pool.destroy()
+
+
+# ------------------------------------------------------------------ planner vs Python model
+
+MB_GROUP, SG_TILE = 8, 64
+
+
+def _even_split(toks, cap):
+    n = len(toks)
+    g = -(-n // cap)
+    b, e = divmod(n, g)
+    out, at = [], 0
+    for i in range(g):
+        m = b + (1 if i < e else 0)
+        out.append(toks[at:at + m])
+        at += m
+    return out
+
+
+def model_plan(wl, base, policy):
+    """Independent model of the grouping: returns [(family, adapter, [tokens])] in dispatch order."""
+    so, sa, ta = wl.seg_offsets, wl.seg_adapter, wl.token_adapter
+    seg_end = int(so[-1])
+    live = lambda a: a >= 0 and wl.ranks[a] > 0
+    mb, sg, sg_ids = [], [], []
+    for s in range(len(sa)):
+        toks = list(range(int(so[s]), int(so[s + 1])))
+        a = int(sa[s])
+        if not toks or not live(a):
+            continue
+        if policy == _lib.POLICY_MBGMV:
+            mb += [(a, t) for t in toks]
+        else:
+            sg += [(a, c) for c in _even_split(toks, SG_TILE)]
+    for q, a in enumerate(ta):
+        a = int(a)
+        if not live(a):
+            continue
+        (sg_ids if policy == _lib.POLICY_SGMV else mb).append((a, seg_end + q))
+    def buckets(pairs, cap):
+        pairs = sorted(pairs, key=lambda p: p[0])  # stable
+        out = []
+        for a in sorted(set(p[0] for p in pairs)):
+            toks = [t for b, t in pairs if b == a]
+            out += [(a, c) for c in _even_split(toks, cap)]
+        return out
+    mbg = buckets(mb, MB_GROUP)
+    sg = sg + buckets(sg_ids, SG_TILE)
+    key = lambda g: -int(wl.ranks[g[0]])
+    mbg = sorted(mbg, key=key)
+    sg = sorted(sg, key=key)
+    return [(0, a, t) for a, t in mbg] + [(1, a, t) for a, t in sg]
+
+
+@pytest.mark.parametrize("wl_name,policy", [
+    ("tiny_decode", _lib.POLICY_AUTO), ("decode_7b", _lib.POLICY_AUTO),
+    ("decode_7b", _lib.POLICY_SGMV), ("mixed_13b", _lib.POLICY_AUTO),
+    ("mixed_13b", _lib.POLICY_MBGMV), ("mixed_13b", _lib.POLICY_SGMV),
+    ("prefill_sgmv", _lib.POLICY_AUTO), ("random", _lib.POLICY_AUTO),
+    ("random", _lib.POLICY_MBGMV), ("random", _lib.POLICY_SGMV)])
+def test_plan_matches_model(wl_name, policy):
+    if wl_name == "random":
+        wl = workloads.random_small(77, n_tokens=150, n_segments=7, rank_choices=(0, 2, 8, 16),
+                                    n_adapters=9, p_none=0.2)
+    else:
+        wl = workloads.make(wl_name)
+    call, pool, pt, base = _call(wl, policy)
+    groups, toks = _lib.plan_inspect(call)
+    model = model_plan(wl, base, policy)
+    assert len(groups) == len(model)
+    slot = 0
+    for (fam, first, n, pt_base, rank), (mfam, ma, mtoks) in zip(groups, model):
+        assert fam == mfam and n == len(mtoks) and first == slot
+        assert pt_base == base[ma] and rank == wl.ranks[ma]
+        assert list(toks[first:first + n]) == mtoks
+        slot += n
+    # every routed token exactly once
+    ids = np.concatenate([np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets)), wl.token_adapter])
+    routed = np.nonzero((ids >= 0) & (wl.ranks[np.maximum(ids, 0)] > 0))[0]
+    assert np.array_equal(np.sort(toks), routed)
+    pool.destroy()
