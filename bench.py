@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the heterogeneous batched LoRA path on one MI355X.
+
+One step = one apply over every projection of the workload (plan on the host,
+work-list upload, shrink and expand kernels) for the whole token batch, adapters
+already resident in HBM. The default workload is the Llama-7B-shape decode batch:
+256 decode tokens, one 4096 -> 4096 projection, Zipf(1.0) routing over 1000
+adapters with ranks in {8, 16, 32, 64}, fp16.
+
+Steps rotate over --instances independent copies of the workload (own pool, own
+pages, own x / y), about 0.5 GiB each, so the 256 MB Infinity Cache cannot hold
+the weights of the instance being timed: the kernels read adapter pages from HBM.
+
+Printed: one JSON line on stdout (tokens/s, roofline of the dominant kernel from
+HIP events around its launches, the CPU oracle's rate on the host cores, fetch
+rate). Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16
+METRIC = "LoRA tokens/s + % peak HBM (decode MBGMV), % MFMA peak (prefill SGMV)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(wl, proj, policy):
+    """Per-kernel algorithmic bytes and flops of one apply of projection `proj`.
+
+    Weights of every distinct active adapter are read once; x is read once, y0 read
+    and y written once. Intermediates (v), page tails and work lists are not counted.
+    Tokens routed by segment go to SGMV under the default policy, per-token ids to
+    MBGMV; the policies override that split."""
+    p = wl.projections[proj]
+    e = 2
+    seg_ids = np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets))
+    fam = {"mbgmv": [], "sgmv": []}
+    for a in seg_ids:
+        fam["mbgmv" if policy == 1 else "sgmv"].append(int(a))
+    for a in wl.token_adapter:
+        fam["sgmv" if policy == 2 else "mbgmv"].append(int(a))
+    out = {}
+    for f, ids in fam.items():
+        ids = np.array([a for a in ids if a >= 0 and wl.ranks[a] > 0], np.int64)
+        T = ids.size
+        uniq = np.unique(ids)
+        r = wl.ranks[uniq].astype(np.int64)
+        out[f + "_shrink"] = dict(bytes=int(r.sum() * p.d_in * e + T * p.d_in * e),
+                                  flops=int(2 * wl.ranks[ids].astype(np.int64).sum() * p.d_in),
+                                  tokens=int(T), adapters=int(uniq.size))
+        out[f + "_expand"] = dict(bytes=int(r.sum() * p.d_out * e + 2 * T * p.d_out * e),
+                                  flops=int(2 * wl.ranks[ids].astype(np.int64).sum() * p.d_out),
+                                  tokens=int(T), adapters=int(uniq.size))
+        out[f + "_fused"] = {k: out[f + "_shrink"][k] + out[f + "_expand"][k]
+                             for k in ("bytes", "flops")}
+        out[f + "_fused"].update(tokens=int(T), adapters=int(uniq.size))
+    return out
+
+
+def load_traffic(kernel, workload):
+    """HBM traffic per launch from a committed rocprofv3 PMC summary, or None when the
+    summary is missing or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    src = os.path.join(ROOT, d["source"])
+    if not os.path.exists(src):
+        return None
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if h != d.get("source_sha256"):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle (fp64 C loops, threads over tokens) on the host cores, on the same
+    workload: full steps while they fit the budget, else a token sample."""
+    import oracle
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    prepared = []
+    T = wl.n_tokens
+    # a token sample when one full step would not fit the budget (cost ~ rank * (d_in + d_out))
+    ids = np.concatenate([np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets)), wl.token_adapter])
+    work = sum(int(wl.ranks[a]) * (p.d_in + p.d_out) for a in ids if a >= 0 for p in wl.projections)
+    est_s = work / (1.5e8 * threads)
+    n_eval = T if est_s < budget_s / 4 else max(16, int(T * (budget_s / 4) / est_s))
+    ev = np.sort(np.random.default_rng(0).choice(T, size=n_eval, replace=False)) if n_eval < T else None
+    for proj in range(len(wl.projections)):
+        p = wl.projections[proj]
+        need = sorted(set(int(a) for a in (ids if ev is None else ids[ev]) if a >= 0 and wl.ranks[a] > 0))
+        adapters = {a: wl.adapter(a, proj) for a in need}
+        pool, pt, base = oracle.build_pool(adapters, wl.n_adapters, p.d_in, p.d_out,
+                                           wl.page_elems, wl.dtype, np.random.default_rng(proj))
+        prepared.append(dict(dtype=wl.dtype, d_in=p.d_in, d_out=p.d_out, x=wl.x(proj),
+                             y0=wl.y0(proj), pool=pool, page_elems=wl.page_elems, page_table=pt,
+                             base=base, rank=wl.ranks, scale=wl.scales, seg_offsets=wl.seg_offsets,
+                             seg_adapter=wl.seg_adapter, token_adapter=wl.token_adapter,
+                             eval_tokens=ev, n_threads=threads))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for kw in prepared:
+            oracle.lora(**kw)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 10000:
+            break
+    tokens = reps * (T if ev is None else ev.size)
+    sample = (f"{reps} full steps ({T} tokens x {len(wl.projections)} projections)" if ev is None
+              else f"{reps} x {ev.size} of {T} tokens (seeded sample) x {len(wl.projections)} projections")
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(el, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode_7b")
+    ap.add_argument("--policy", default="auto", choices=["auto", "mbgmv", "sgmv"])
+    ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would own "
+              "its pool and serve its own requests); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from heterogeneous_lora_amd import _lib, runtime
+
+    _lib.load()
+    policy = {"auto": 0, "mbgmv": 1, "sgmv": 2}[args.policy]
+    wl = workloads.make(args.config)
+    T = wl.n_tokens
+    n_proj = len(wl.projections)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {wl.name}: {wl.description}")
+    active = [int(a) for a in wl.active_adapters()]
+    log(f"[bench] {T} tokens, {len(active)} active adapters, {n_proj} projection(s)")
+
+    store = runtime.HostStore(wl, active)
+    insts, fetch_ms = [], []
+    for i in range(args.instances):
+        inst = runtime.PagedLoRA(wl, device="cuda:0", store=store, pool_seed=wl.pool_seed + i)
+        fetch_ms.append(inst.fetch_ms)
+        calls = [inst.call(p, policy) for p in range(n_proj)]
+        io = [inst.inputs(p) for p in range(n_proj)]
+        ws = torch.zeros(max(_lib.workspace_size(c) for c in calls), dtype=torch.uint8, device=dev)
+        insts.append((inst, calls, io, ws))
+        log(f"[bench] instance {i} ready (fetch {inst.fetch_ms:.2f} ms)")
+    fetch_bytes = sum(int(wl.ranks[a]) * (p.d_in + p.d_out) * 2 for a in active
+                      for p in wl.projections)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        inst, calls, io, ws = insts[i % len(insts)]
+        for p in range(n_proj):
+            inst.apply(calls[p], io[p][0], io[p][1], ws, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    _lib.timing_enable(True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    timing = _lib.timing_read()
+    _lib.timing_enable(False)
+    wall = t1 - t0
+    ms_per_step = wall / args.steps * 1e3
+    value = T * args.steps / wall
+    log(f"[bench] {args.steps} steps in {wall:.4f} s: {ms_per_step * 1e3:.1f} us/step, "
+        f"{value:.4g} tokens/s")
+
+    # per-kernel roofline (bytes and flops averaged over the projections' launches)
+    alg = [algorithmic(wl, p, policy) for p in range(n_proj)]
+    kernels = {}
+    for k, (n, ms) in timing.items():
+        if n == 0:
+            continue
+        per_launch_bytes = float(np.mean([a[k]["bytes"] for a in alg]))
+        per_launch_flops = float(np.mean([a[k]["flops"] for a in alg]))
+        avg_s = ms / n * 1e-3
+        kernels[k] = {"launches": n, "avg_us": round(avg_s * 1e6, 3),
+                      "algorithmic_bytes": int(per_launch_bytes),
+                      "gbps": round(per_launch_bytes / avg_s / 1e9, 1),
+                      "tflops": round(per_launch_flops / avg_s / 1e12, 3)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    dk = kernels[dom]
+    sgmv_like = dom.startswith("sgmv")
+    traffic = load_traffic(dom, wl.name)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["gbps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    if sgmv_like:
+        roofline["mfma_frac"] = round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
+    kern_total_s = sum(ms for n, ms in timing.values()) * 1e-3 / args.steps
+    step_bytes = sum(sum(v["bytes"] for v in a.values()) for a in alg)
+    log(f"[bench] kernels: {json.dumps(kernels)}")
+    log(f"[bench] all kernels of a step: {kern_total_s * 1e6:.1f} us, "
+        f"{step_bytes / kern_total_s / 1e9:.0f} GB/s algorithmic")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu}")
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "projections": n_proj,
+                   "shape": [[p.d_in, p.d_out] for p in wl.projections],
+                   "active_adapters": len(active), "policy": args.policy,
+                   "instances_rotated": args.instances, "accumulate": "f32",
+                   "page_elems": wl.page_elems, "pool_pages": wl.n_pages},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "step_kernel_us": round(kern_total_s * 1e6, 2),
+        "step_algorithmic_gbps": round(step_bytes / kern_total_s / 1e9, 1),
+        "fetch": {"bytes": fetch_bytes, "ms": round(float(np.median(fetch_ms)), 3),
+                  "gbps": round(fetch_bytes / (float(np.median(fetch_ms)) * 1e-3) / 1e9, 2)},
+    }
+    for inst, *_ in insts:
+        inst.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -73,6 +73,9 @@ def load(path: str = LIB_PATH):
         "slora_expand": ([P, P, P, P, P, _c_i64, P], I),
         "slora_apply": ([P, P, P, P, P, _c_i64, P], I),
         "slora_plan_inspect": ([P, P, P, P, I, P], I),
+        "slora_timing_enable": ([I], I),
+        "slora_workspace_status": ([P, P, P], I),
+        "slora_timing_read": ([I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -212,6 +215,29 @@ def expand(call: Call, v: int, y: int, ws: int, ws_bytes: int, stream: int):
 def apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
     _check(load().slora_apply(ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(x), _vp(y),
                               _vp(ws), ws_bytes, _vp(stream)), "apply")
+
+
+KERNELS = ["mbgmv_shrink", "mbgmv_expand", "sgmv_shrink", "sgmv_expand", "mbgmv_fused"]
+
+
+def timing_enable(on: bool):
+    _check(load().slora_timing_enable(1 if on else 0), "timing_enable")
+
+
+def timing_read():
+    """{kernel name: (launches, total ms)} since timing_enable; clears the counters."""
+    n = len(KERNELS)
+    launches = np.zeros(n, np.int64)
+    ms = np.zeros(n, np.float64)
+    _check(load().slora_timing_read(n, _p(launches), _p(ms)), "timing_read")
+    return {k: (int(launches[i]), float(ms[i])) for i, k in enumerate(KERNELS)}
+
+
+def workspace_status(ws: int, stream: int) -> int:
+    """0 if the last call on this workspace ran clean (synchronizes the stream)."""
+    st = _c_i32()
+    _check(load().slora_workspace_status(_vp(ws), _vp(stream), ctypes.byref(st)), "workspace_status")
+    return st.value
 
 
 def plan_inspect(call: Call):

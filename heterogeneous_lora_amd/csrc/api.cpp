@@ -1,12 +1,14 @@
-// Compute entry points: validate, plan on the host, upload the work list into the
-// caller's workspace through a pinned staging ring, launch the kernels.
+// Compute entry points: validate and plan on the host straight into a pinned
+// staging buffer, then launch the kernels, which read the work list from that
+// buffer over the bus (no separate upload, no device staging).
 //
-// Decode tokens go to MBGMV (page-gathered GEMV groups), prefill segments to SGMV
-// (MFMA tiles), per the split between the memory-bound decode phase and the
-// parallel, compute-heavy prefill phase ("vLLM ile cikarimi olceklemek", the
-// prefill / decode paragraphs).
+// Decode tokens go to MBGMV (page-gathered GEMV groups, shrink and expand in one
+// launch), prefill segments to SGMV (MFMA tiles), following the split between the
+// memory-bound decode phase and the parallel, compute-heavy prefill phase ("vLLM
+// ile cikarimi olceklemek", the prefill / decode paragraphs).
 #include <string.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 
@@ -16,28 +18,29 @@ using namespace slora;
 
 namespace {
 
-// Pinned staging ring for work lists. A slot is reused only after the copy that
-// last read it has completed (its event), so the host never overwrites a buffer a
-// pending hipMemcpyAsync still reads.
+// Pinned staging ring. A slot is written by the host only after the kernels that
+// read the previous plan in it have finished (its event).
 struct StagingSlot {
   void* host = nullptr;
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   bool pending = false;
 };
-constexpr int kSlots = 8;
+constexpr int kSlots = 16;
 struct Ring {
   StagingSlot slot[kSlots];
   int next = 0;
 };
-std::mutex g_ring_mu;
-std::map<int, Ring> g_rings;  // per device
+std::mutex g_mu;  // guards the rings, the epoch map and the timing state
+std::map<int, Ring> g_rings;                 // per device
+std::map<const void*, uint64_t> g_ws_epoch;  // last epoch a fused call used per workspace
+std::atomic<uint64_t> g_epoch{0};
+thread_local PlanScratch t_scratch;
 
-int upload(const void* src, size_t n, void* dst, hipStream_t stream) {
+int acquire_slot(size_t n, StagingSlot** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lk(g_ring_mu);
   Ring& ring = g_rings[dev];
   StagingSlot& s = ring.slot[ring.next];
   ring.next = (ring.next + 1) % kSlots;
@@ -60,13 +63,41 @@ int upload(const void* src, size_t n, void* dst, hipStream_t stream) {
     if (e != hipSuccess) { s.host = nullptr; return hip_fail(e, "staging: hipHostMalloc"); }
     s.cap = cap;
   }
-  memcpy(s.host, src, n);
-  e = hipMemcpyAsync(dst, s.host, n, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "staging: hipMemcpyAsync");
-  e = hipEventRecord(s.ev, stream);
-  if (e != hipSuccess) return hip_fail(e, "staging: hipEventRecord");
-  s.pending = true;
+  *out = &s;
   return SLORA_OK;
+}
+
+// Kernel timing: event pairs around launches while enabled (benchmarks only).
+struct TimedLaunch {
+  int kernel;
+  hipEvent_t start, stop;
+};
+bool g_timing_on = false;
+std::vector<TimedLaunch> g_timed;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_spare_events;
+
+template <typename F>
+hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
+  if (!g_timing_on) return launch();
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (!g_spare_events.empty()) {
+    ev = g_spare_events.back();
+    g_spare_events.pop_back();
+  } else {
+    hipError_t e = hipEventCreate(&ev.first);
+    if (e != hipSuccess) return e;
+    e = hipEventCreate(&ev.second);
+    if (e != hipSuccess) { (void)hipEventDestroy(ev.first); return e; }
+  }
+  hipError_t e = hipEventRecord(ev.first, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(ev.second, s);
+  if (e != hipSuccess) {
+    g_spare_events.push_back(ev);
+    return e;
+  }
+  g_timed.push_back({kernel, ev.first, ev.second});
+  return hipSuccess;
 }
 
 enum Mode { kShrink = 1, kExpand = 2, kApply = 3 };
@@ -76,9 +107,9 @@ bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out,
         const float* v_in, void* y, void* ws, int64_t ws_bytes, void* stream, int mode) {
   clear_error();
-  Plan plan;
-  int rc = validate_and_plan(L, R, &plan);
-  if (rc) return rc;
+  PlanView pv;
+  const int64_t bytes = plan_bytes(L, R, &t_scratch, &pv);
+  if (bytes < 0) return (int)bytes;
   if ((mode & kShrink) && (!x || misaligned(x, 16)))
     return fail(SLORA_E_INVALID, "x must be a 16-byte aligned device pointer");
   if ((mode & kExpand) && (!y || misaligned(y, 16)))
@@ -87,26 +118,21 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
     return fail(SLORA_E_INVALID, "v must be a 16-byte aligned device pointer");
   if (mode == kExpand && (!v_in || misaligned(v_in, 16)))
     return fail(SLORA_E_INVALID, "v must be a 16-byte aligned device pointer");
-  const PlanLayout lay = layout_plan(L, R, plan);
+  const WsLayout lay = ws_layout(L, R, pv.n_groups);
   if (!ws || misaligned(ws, 256)) return fail(SLORA_E_INVALID, "ws must be 256-byte aligned");
   if (ws_bytes < lay.total)
     return fail(SLORA_E_INVALID, "workspace of %lld bytes is smaller than the %lld needed",
                 (long long)ws_bytes, (long long)lay.total);
-  if (plan.n_routed == 0) return SLORA_OK;
+  if (pv.n_routed == 0) return SLORA_OK;
 
-  std::vector<uint8_t> blob((size_t)lay.blob_bytes, 0);
-  auto put = [&](int64_t off, const void* src, size_t n) {
-    if (n) memcpy(blob.data() + (off - lay.blob_off), src, n);
-  };
-  put(lay.tok_off, plan.tok.data(), plan.tok.size() * 4);
-  put(lay.mbg_off, plan.mb_groups.data(), plan.mb_groups.size() * sizeof(GroupDesc));
-  put(lay.mbs_off, plan.mb_shrink.data(), plan.mb_shrink.size() * sizeof(Item));
-  put(lay.sgt_off, plan.sg_tiles.data(), plan.sg_tiles.size() * sizeof(GroupDesc));
+  std::lock_guard<std::mutex> lk(g_mu);
+  StagingSlot* slot = nullptr;
+  int rc = acquire_slot((size_t)bytes, &slot);
+  if (rc) return rc;
+  plan_write(L, R, &t_scratch, slot->host, &pv);  // kernels read this host buffer directly
+
   hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)ws;
-  rc = upload(blob.data(), blob.size(), wsb + lay.blob_off, s);
-  if (rc) return rc;
-
   Geom g;
   g.pool = (const uint16_t*)L->pool;
   g.n_pages = L->n_pages;
@@ -118,35 +144,43 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
   g.cB = (L->d_out + g.P - 1) / g.P;
   g.pt = L->page_table;
   g.r_max = L->r_max;
-  const int32_t* tok = (const int32_t*)(wsb + lay.tok_off);
-  const GroupDesc* mbg = (const GroupDesc*)(wsb + lay.mbg_off);
-  const Item* mbs = (const Item*)(wsb + lay.mbs_off);
-  const GroupDesc* sgt = (const GroupDesc*)(wsb + lay.sgt_off);
+  unsigned long long* counters = (unsigned long long*)(wsb + lay.cnt_off);
+  unsigned long long* err = (unsigned long long*)wsb;
   float* v = mode == kApply ? (float*)(wsb + lay.v_off) : (mode == kShrink ? v_out : nullptr);
   const float* vr = mode == kApply ? v : v_in;
-  const int32_t n_mbg = (int32_t)plan.mb_groups.size(), n_mbs = (int32_t)plan.mb_shrink.size();
-  const int32_t n_sgt = (int32_t)plan.sg_tiles.size();
-  hipError_t e;
-  if (mode & kShrink) {
-    if (n_sgt) {
-      e = launch_sgmv_shrink(g, tok, sgt, n_sgt, x, v, s);
-      if (e != hipSuccess) return hip_fail(e, "sgmv_shrink launch");
-    }
-    if (n_mbs) {
-      e = launch_mbgmv_shrink(g, tok, mbg, mbs, n_mbs, x, v, s);
-      if (e != hipSuccess) return hip_fail(e, "mbgmv_shrink launch");
-    }
+  hipError_t e = hipSuccess;
+  if (pv.n_sg && (mode & kShrink)) {
+    e = timed_launch(SLORA_K_SGMV_SHRINK, s, [&] { return launch_sgmv_shrink(g, pv.tok, pv.sg, pv.n_sg, x, v, s); });
+    if (e != hipSuccess) return hip_fail(e, "sgmv_shrink launch");
   }
-  if (mode & kExpand) {
-    if (n_sgt) {
-      e = launch_sgmv_expand(g, tok, sgt, n_sgt, vr, y, s);
-      if (e != hipSuccess) return hip_fail(e, "sgmv_expand launch");
-    }
-    if (n_mbg) {
-      e = launch_mbgmv_expand(g, tok, mbg, n_mbg, vr, y, s);
-      if (e != hipSuccess) return hip_fail(e, "mbgmv_expand launch");
-    }
+  if (pv.n_sg && (mode & kExpand)) {
+    e = timed_launch(SLORA_K_SGMV_EXPAND, s, [&] { return launch_sgmv_expand(g, pv.tok, pv.sg, pv.n_sg, vr, y, s); });
+    if (e != hipSuccess) return hip_fail(e, "sgmv_expand launch");
   }
+  if (pv.n_mb) {
+    if (mode == kApply) {
+      const unsigned long long epoch = ++g_epoch;
+      g_ws_epoch[ws] = epoch;
+      e = timed_launch(SLORA_K_MBGMV_FUSED, s, [&] {
+        return launch_mbgmv(g, pv.mb, pv.n_mb, pv.n_mb_shrink, pv.mb_max_tok, x, v, y, counters,
+                            epoch, err, s);
+      });
+    } else if (mode == kShrink) {
+      e = timed_launch(SLORA_K_MBGMV_SHRINK, s, [&] {
+        return launch_mbgmv(g, pv.mb, pv.n_mb_shrink, pv.n_mb_shrink, pv.mb_max_tok, x, v, nullptr,
+                            counters, 0, err, s);
+      });
+    } else {
+      e = timed_launch(SLORA_K_MBGMV_EXPAND, s, [&] {
+        return launch_mbgmv(g, pv.mb + pv.n_mb_shrink, pv.n_mb - pv.n_mb_shrink, 0, pv.mb_max_tok,
+                            nullptr, const_cast<float*>(vr), y, counters, 0, err, s);
+      });
+    }
+    if (e != hipSuccess) return hip_fail(e, "mbgmv launch");
+  }
+  e = hipEventRecord(slot->ev, s);
+  if (e != hipSuccess) return hip_fail(e, "staging: hipEventRecord");
+  slot->pending = true;
   return SLORA_OK;
 }
 
@@ -154,10 +188,54 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
 
 extern "C" {
 
+int slora_timing_enable(int32_t on) {
+  clear_error();
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_timing_on = on != 0;
+  for (auto& t : g_timed) g_spare_events.push_back({t.start, t.stop});
+  g_timed.clear();
+  return SLORA_OK;
+}
+
+int slora_timing_read(int32_t n_kernels, int64_t* launches, double* total_ms) {
+  clear_error();
+  if (n_kernels < 0 || n_kernels > SLORA_K_COUNT || (n_kernels > 0 && (!launches || !total_ms)))
+    return fail(SLORA_E_INVALID, "timing_read: bad arguments");
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (int32_t k = 0; k < n_kernels; ++k) { launches[k] = 0; total_ms[k] = 0.0; }
+  int rc = SLORA_OK;
+  for (auto& t : g_timed) {
+    hipError_t e = hipEventSynchronize(t.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess && rc == SLORA_OK) rc = hip_fail(e, "timing_read");
+    if (t.kernel < n_kernels) {
+      launches[t.kernel] += 1;
+      total_ms[t.kernel] += ms;
+    }
+    g_spare_events.push_back({t.start, t.stop});
+  }
+  g_timed.clear();
+  return rc;
+}
+
 int slora_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes) {
   clear_error();
   if (!lora || !routing || !bytes) return fail(SLORA_E_INVALID, "workspace_size: NULL argument");
   *bytes = workspace_bound(lora, routing);
+  return SLORA_OK;
+}
+
+int slora_workspace_status(const void* ws, void* stream, int32_t* status) {
+  clear_error();
+  if (!ws || !status) return fail(SLORA_E_INVALID, "workspace_status: NULL argument");
+  unsigned long long flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, ws, sizeof flag, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "workspace_status");
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_ws_epoch.find(ws);
+  *status = (it != g_ws_epoch.end() && flag == it->second) ? 1 : 0;
   return SLORA_OK;
 }
 
@@ -171,35 +249,53 @@ int slora_expand(const slora_lora* lora, const slora_routing* routing, const flo
   return run(lora, routing, nullptr, nullptr, v, y, ws, ws_bytes, stream, kExpand);
 }
 
+int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
+                void* ws, int64_t ws_bytes, void* stream) {
+  return run(lora, routing, x, nullptr, nullptr, y, ws, ws_bytes, stream, kApply);
+}
+
 int slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int32_t* n_groups,
                        int32_t* info, int32_t info_cap, int32_t* tokens) {
   clear_error();
   if (!n_groups) return fail(SLORA_E_INVALID, "plan_inspect: n_groups is NULL");
-  Plan plan;
-  int rc = validate_and_plan(lora, routing, &plan);
-  if (rc) return rc;
-  const int32_t n = (int32_t)(plan.mb_groups.size() + plan.sg_tiles.size());
+  PlanScratch sc;
+  PlanView pv;
+  const int64_t bytes = plan_bytes(lora, routing, &sc, &pv);
+  if (bytes < 0) return (int)bytes;
+  std::vector<uint8_t> buf((size_t)bytes + 64);
+  void* aligned = (void*)(((uintptr_t)buf.data() + 63) & ~(uintptr_t)63);
+  plan_write(lora, routing, &sc, aligned, &pv);
+  const int32_t n = pv.n_groups + pv.n_sg;
   *n_groups = n;
   if (n > info_cap || !info) return fail(SLORA_E_INVALID, "plan_inspect: %d groups > cap %d", n, info_cap);
-  int32_t at = 0;
-  for (int fam = 0; fam < 2; ++fam) {
-    const std::vector<GroupDesc>& gs = fam == 0 ? plan.mb_groups : plan.sg_tiles;
-    for (const GroupDesc& g : gs) {
-      info[5 * at + 0] = fam;
-      info[5 * at + 1] = g.tok_begin;
-      info[5 * at + 2] = g.n_tok;
-      info[5 * at + 3] = g.pt_base;
-      info[5 * at + 4] = g.rank;
-      ++at;
-    }
+  // MBGMV groups from their first shrink item each, in dispatch order
+  int32_t at = 0, slot = 0;
+  for (int32_t i = 0; i < pv.n_mb_shrink; ++i) {
+    const MbItem& it = pv.mb[i];
+    if (it.part != 0) continue;
+    info[5 * at + 0] = 0;
+    info[5 * at + 1] = slot;
+    info[5 * at + 2] = it.n_tok;
+    info[5 * at + 3] = it.pt_base;
+    info[5 * at + 4] = it.rank;
+    if (tokens)
+      for (int32_t t = 0; t < it.n_tok; ++t) tokens[slot + t] = it.tok[t];
+    slot += it.n_tok;
+    ++at;
   }
-  if (tokens && !plan.tok.empty()) memcpy(tokens, plan.tok.data(), plan.tok.size() * 4);
+  for (int32_t i = 0; i < pv.n_sg; ++i) {
+    const SgTile& t = pv.sg[i];
+    info[5 * at + 0] = 1;
+    info[5 * at + 1] = slot;
+    info[5 * at + 2] = t.n_tok;
+    info[5 * at + 3] = t.pt_base;
+    info[5 * at + 4] = t.rank;
+    if (tokens)
+      for (int32_t q = 0; q < t.n_tok; ++q) tokens[slot + q] = pv.tok[t.tok_begin + q];
+    slot += t.n_tok;
+    ++at;
+  }
   return SLORA_OK;
-}
-
-int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
-                void* ws, int64_t ws_bytes, void* stream) {
-  return run(lora, routing, x, nullptr, nullptr, y, ws, ws_bytes, stream, kApply);
 }
 
 }  // extern "C"

@@ -19,6 +19,28 @@ __device__ __forceinline__ uint32_t nan2() {
   return DT == SLORA_F16 ? 0x7E007E00u : 0x7FC07FC0u;
 }
 
+// 16-byte fill vectors in device memory. Loads that must not touch the pool (rows
+// past the rank, an invalid page id, lanes past the end of a row) are pointed at
+// these instead of being predicated, so every load issues unconditionally and no
+// loaded value is selected on before it is used. (Not const, so the compiler
+// cannot fold these loads back into selects on loaded data.)
+struct alignas(16) FillVectors {
+  uint32_t zero[4];
+  uint32_t nan_f16[4];
+  uint32_t nan_bf16[4];
+};
+__device__ FillVectors kFill = {{0u, 0u, 0u, 0u},
+                                      {0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u},
+                                      {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u}};
+
+__device__ __forceinline__ const uint16_t* fill_zero() {
+  return reinterpret_cast<const uint16_t*>(kFill.zero);
+}
+template <int DT>
+__device__ __forceinline__ const uint16_t* fill_nan() {
+  return reinterpret_cast<const uint16_t*>(DT == SLORA_F16 ? kFill.nan_f16 : kFill.nan_bf16);
+}
+
 template <int DT>
 __device__ __forceinline__ float lo_f32(uint32_t w) {
   if constexpr (DT == SLORA_F16)
@@ -72,47 +94,78 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float c) {
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(uint16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
-// Sum V values per lane across the 64 lanes of a wave. Halving butterfly: at each
-// step a lane trades the half of its values its partner keeps, so V values need
-// V - 1 exchanges plus log2(64 / V) for the tail, instead of 6 V. Lane l returns
-// the total of value index reduce_index<V>(l); lanes l and l ^ m for the tail masks
-// m < 64 / V return the same total. The summation order is fixed by lane numbers.
+// Sum V values per lane (V a power of two, 1..64) over the 64 lanes of a wave,
+// with no per-lane selects (which the compiler would turn into indexed scratch):
+//   * v_permlane32_swap pairs value i with value i + V/2 across the lane halves:
+//     after "swap(a[i], a[i + V/2]); a[i] = a[i] + a[i + V/2]", lanes 0-31 hold
+//     the sum over (l, l ^ 32) of value i and lanes 32-63 that of value i + V/2;
+//   * v_permlane16_swap does the same between rows 2j and 2j + 1 (16 lanes each);
+//   * a DPP reduction inside each row of 16 lanes (rotate by 8 and 4, then quad
+//     permutations) completes the sum.
+// With one value left, a register is swapped with itself, which adds the two
+// halves. Afterwards lane l holds in out[i] the total of value wave_sum_index<V>(l, i),
+// replicated across every lane that wave_sum_writer<V> does not select. The order of
+// the additions depends on lane numbers only, so results are reproducible.
 template <int V>
-__device__ __forceinline__ float xreduce(float (&a)[V], int lane) {
+struct WaveSum {
   static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
-  int m = 32;
-#pragma unroll
-  for (int h = V / 2; h >= 1; h /= 2) {
-    const bool up = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < h; ++i) {
-      const float send = up ? a[i] : a[i + h];
-      const float keep = up ? a[i + h] : a[i];
-      a[i] = keep + __shfl_xor(send, m);
-    }
-    m >>= 1;
-  }
-  float r = a[0];
-#pragma unroll
-  for (; m >= 1; m >>= 1) r += __shfl_xor(r, m);
-  return r;
+  static constexpr int kOut = V >= 4 ? V / 4 : 1;
+};
+
+__device__ __forceinline__ void swap_add32(float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  lo = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap_add16(float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  lo = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
 
 template <int V>
-__device__ __forceinline__ int reduce_index(int lane) {
-  int idx = 0, m = 32;
+__device__ __forceinline__ void wave_sum(float (&a)[V], float (&out)[WaveSum<V>::kOut]) {
+  constexpr int K = WaveSum<V>::kOut;
+  if constexpr (V >= 2) {
 #pragma unroll
-  for (int h = V / 2; h >= 1; h /= 2) {
-    if (lane & m) idx += h;
-    m >>= 1;
+    for (int i = 0; i < V / 2; ++i) swap_add32(a[i], a[i + V / 2]);
+  } else {
+    float t = a[0];
+    swap_add32(a[0], t);
   }
-  return idx;
+  if constexpr (V >= 4) {
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) swap_add16(a[i], a[i + V / 4]);
+  } else {
+    float t = a[0];
+    swap_add16(a[0], t);
+  }
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    float x = a[i];
+    x = dpp_add<0x128>(x);  // row_ror:8
+    x = dpp_add<0x124>(x);  // row_ror:4
+    x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+    x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+    out[i] = x;
+  }
 }
 
-// lanes that write the reduced values (one per index)
 template <int V>
-__device__ __forceinline__ bool reduce_writer(int lane) {
-  return (lane & (64 / V - 1)) == 0;
+__device__ __forceinline__ int wave_sum_index(int lane, int i) {
+  int base = 0;
+  if constexpr (V >= 2) base += ((lane >> 5) & 1) * (V / 2);
+  if constexpr (V >= 4) base += ((lane >> 4) & 1) * (V / 4);
+  return base + i;
+}
+
+template <int V>
+__device__ __forceinline__ bool wave_sum_writer(int lane, int i) {
+  if constexpr (V >= 4) return (lane & 15) == i;
+  else if constexpr (V == 2) return (lane & 31) == 0;
+  else return lane == 0;
 }
 
 }  // namespace dev

@@ -17,30 +17,45 @@ int hip_fail(hipError_t e, const char* what);
 void clear_error();
 
 // ---------------------------------------------------------------- work lists
-// Granularity of the work lists (the planner and the kernels agree on these).
-constexpr int kMaxRank = 128;     // largest rank the kernels accept (r_max <= kMaxRank)
-constexpr int kMbGroup = 8;       // MBGMV: tokens per group (one read of the adapter per group)
-constexpr int kMbShrinkRows = 8;  // MBGMV shrink: A^T rows per workgroup (4 waves x 2 rows)
-constexpr int kMbExpandCols = 1024;  // MBGMV expand: output columns per workgroup (2 waves x 512)
-constexpr int kSgTile = 64;       // SGMV: tokens per tile (M of the MFMA tiles)
-constexpr int kSgExpandCols = 256;   // SGMV expand: output columns per workgroup
+constexpr int kMaxRank = 128;       // largest rank the kernels accept (r_max <= kMaxRank)
+constexpr int kMbGroup = 4;         // MBGMV: tokens per group (one read of the adapter per group)
+constexpr int kMbShrinkRows = 8;    // MBGMV shrink: A^T rows per workgroup (4 waves x 2 rows)
+constexpr int kMbExpandTok = 2;     // MBGMV expand: tokens per workgroup
+constexpr int kMbWaveCols = 512;    // MBGMV expand: output columns per wave (64 lanes x 8)
+constexpr int kMbRowsPerWave = 16;  // MBGMV expand: B rows a wave keeps in flight
+constexpr int kSgTile = 64;         // SGMV: tokens per tile
 
-// One group of tokens that share an adapter (MBGMV group or SGMV tile). 32 bytes.
-struct GroupDesc {
+// Expand waves that split one column slice's rows: 1, 2 or 4 (4 waves per workgroup).
+inline int mb_split(int rank) { return rank <= 16 ? 1 : rank <= 32 ? 2 : 4; }
+
+// One MBGMV work item (one workgroup), 64 bytes, read by the kernel straight from
+// the pinned staging buffer. Token ids are inline so a workgroup needs one load to
+// know all it has to read.
+struct MbItem {
+  int32_t tok[kMbGroup];  // token ids (n_tok of them)
+  int32_t n_tok;
+  int32_t pt_base;        // page-table entry of the adapter's A^T row 0, chunk 0
+  int32_t rank;
+  float scale;
+  int32_t role;           // 0 = shrink, 1 = expand
+  int32_t part;           // shrink: row block; expand: column tile
+  int32_t split;          // expand: waves sharing a column slice (mb_split(rank))
+  int32_t group;          // completion counter slot of the item's group
+  int32_t need;           // expand: shrink items of the group
+  int32_t pad[3];
+};
+static_assert(sizeof(MbItem) == 64, "MbItem layout");
+
+// One SGMV tile: up to kSgTile tokens of one adapter. 32 bytes.
+struct SgTile {
   int32_t tok_begin;  // first index into the token list
-  int32_t n_tok;      // tokens in the group (1..kMbGroup or 1..kSgTile)
-  int32_t pt_base;    // page-table entry of the adapter's A^T row 0, chunk 0
-  int32_t rank;       // r (>= 1)
-  float scale;        // s
-  int32_t pad0, pad1, pad2;
+  int32_t n_tok;
+  int32_t pt_base;
+  int32_t rank;
+  float scale;
+  int32_t pad[3];
 };
-static_assert(sizeof(GroupDesc) == 32, "GroupDesc layout");
-
-// (group, block) work item: row block for shrink kernels.
-struct Item {
-  int32_t group;
-  int32_t block;
-};
+static_assert(sizeof(SgTile) == 32, "SgTile layout");
 
 // Geometry of one projection, as the kernels see it.
 struct Geom {
@@ -54,36 +69,55 @@ struct Geom {
   int32_t r_max;
 };
 
-// Host-side plan; copied as one blob into the workspace.
-struct Plan {
-  std::vector<int32_t> tok;           // token ids, grouped
-  std::vector<GroupDesc> mb_groups;   // MBGMV groups (rank-descending order)
-  std::vector<Item> mb_shrink;        // (group, row block)
-  std::vector<GroupDesc> sg_tiles;    // SGMV tiles (rank-descending order)
+// Host plan of one call, built straight into a pinned staging buffer:
+// [MbItem x n_mb][SgTile x n_sg][int32 tokens x n_tok]
+struct PlanView {
+  MbItem* mb = nullptr;
+  int32_t n_mb = 0, n_mb_shrink = 0, n_groups = 0;
+  SgTile* sg = nullptr;
+  int32_t n_sg = 0;
+  int32_t* tok = nullptr;
+  int32_t n_tok = 0;
   int32_t n_routed = 0;
+  int32_t mb_max_tok = 0;
 };
 
-// Byte offsets of the plan sections inside the workspace (after v).
-struct PlanLayout {
-  int64_t v_off, v_bytes;
-  int64_t tok_off, mbg_off, mbs_off, sgt_off;
-  int64_t blob_off, blob_bytes;  // [blob_off, blob_off + blob_bytes) is copied from the host
-  int64_t total;
+// Scratch the planner reuses between calls (thread-local, grows only).
+struct PlanScratch {
+  std::vector<uint64_t> mb_keys, sg_keys;    // (adapter << 32 | token), sorted
+  std::vector<int32_t> grp;                  // MBGMV groups: (key index, count, adapter) triples
+  std::vector<int32_t> tiles;                // SGMV tiles: (first token or key index, count, adapter, from-keys)
+  std::vector<int32_t> order, tile_order, tiles_sorted;
 };
 
-int validate_and_plan(const slora_lora* L, const slora_routing* R, Plan* plan);
+// Validate, group and count; returns the bytes the plan needs, or a negative
+// SLORA_E_* code. counts gets the sizes.
+int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc, PlanView* counts);
+// Write the plan into buf (plan_bytes bytes, 64-byte aligned) from the state plan_bytes left.
+void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, void* buf,
+                PlanView* out);
+
+// Workspace (device, caller-owned, zero-filled once at allocation):
+//   [0, 256): header: uint64 epoch of the last failed wait
+//   [256, ...): uint64 completion counter per MBGMV group
+//   then v: float [n_tokens x r_max]
+constexpr int64_t kHeaderBytes = 256;
 int64_t workspace_bound(const slora_lora* L, const slora_routing* R);
-PlanLayout layout_plan(const slora_lora* L, const slora_routing* R, const Plan& p);
+struct WsLayout {
+  int64_t cnt_off, v_off, total;
+};
+WsLayout ws_layout(const slora_lora* L, const slora_routing* R, int32_t n_groups);
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_mbgmv_shrink(const Geom& g, const int32_t* tok, const GroupDesc* groups,
-                               const Item* items, int32_t n_items, const void* x, float* v,
-                               hipStream_t s);
-hipError_t launch_mbgmv_expand(const Geom& g, const int32_t* tok, const GroupDesc* groups,
-                               int32_t n_groups, const float* v, void* y, hipStream_t s);
-hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const GroupDesc* tiles,
+// items[0, n_shrink) shrink, the rest expand. epoch != 0 makes the launch a fused
+// apply: shrink items publish their group's counter, expand items wait for it.
+hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, int32_t n_shrink,
+                        int32_t max_tok, const void* x, float* v, void* y,
+                        unsigned long long* counters, unsigned long long epoch,
+                        unsigned long long* err, hipStream_t s);
+hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, const void* x, float* v, hipStream_t s);
-hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const GroupDesc* tiles,
+hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, const float* v, void* y, hipStream_t s);
 
 constexpr int kFetchMaxPages = 240;

@@ -4,18 +4,44 @@
 // its own adapter; the S-LoRA overview, section "2. Heterogeneous Batching":
 // kernels that work on non-contiguous memory and on mixed ranks at once).
 //
-// Decode is memory bound: each adapter row is read once per group of up to
-// kMbGroup tokens sharing the adapter, so the kernels stream adapter pages from
-// HBM with 16-byte loads per lane (a wave reads 1 KiB of one page per load
-// instruction) and keep the arithmetic in registers.
+// One kernel runs both halves of the LoRA product so that a decode batch is a
+// single launch (a decode batch moves tens of MB; two launches would each pay the
+// fixed launch and ramp cost, which is of the order of the whole transfer). The
+// work list (64-byte items, token ids inline) is read from pinned host memory.
 //
-// shrink: one workgroup = (group, block of 8 rows of A^T); each wave owns 2 rows.
-//         Lanes hold 8-element slices of a row, dot them with the group's x rows
-//         (v_dot2 fp16/bf16 -> fp32), and one halving butterfly reduces all
-//         2 x kMbGroup partial sums of the wave at once. v is written in fp32.
-// expand: one workgroup = (group, 1024 output columns); v of the group is staged
-//         in LDS, each lane streams 16 bytes of each B row, accumulates
-//         kMbGroup x 8 fp32 sums over k, then y = RNE(y0 + s * acc) in place.
+//   shrink items (first in the grid): (group of <= 4 tokens, 8 rows of A^T),
+//     4 waves x 2 rows. The group's x goes straight from global memory into LDS
+//     (global_load_lds_dwordx4); each wave loads its 2 rows (4096 elements per
+//     batch) with one 16-byte load per lane and slice, dots them with every
+//     token's x (v_dot2 fp16/bf16 -> fp32) and reduces all 2 x G lane partial
+//     sums at once (permlane swaps + DPP). v is stored with agent-scope stores;
+//     once they have completed, the workgroup advances the group's counter.
+//   expand items: (<= 2 tokens of a group, 2048 / split output columns). The 4
+//     waves cover 4 / split slices of 512 columns; the `split` waves of a slice
+//     share its rows (split = 1, 2, 4 for rank <= 16, <= 32, more), so no wave
+//     holds more than 16 B rows in flight and none walks a long chain of loads.
+//     Each wave loads its page ids, prefetches y0 and issues its B rows before it
+//     waits for the group's counter; then v arrives (agent-scope loads, lane k
+//     holds v[t][k]) and is read with v_readlane; acc[t][8] accumulates in fp32;
+//     the waves of a slice add their partial sums through LDS in a fixed order,
+//     and y = RNE(y0 + s * acc).
+//
+// Memory ordering: v is written and read with relaxed agent-scope atomics (sc1:
+// performed at the agent coherence point); a writer waits for its stores to
+// complete (s_waitcnt) before the barrier that precedes the counter update, and
+// a reader issues its v loads only after it has observed the counter, so neither
+// side needs an L2 write-back or invalidation. Counters hold (epoch << 16) | count
+// and need no reset between calls (the workspace starts zeroed once).
+//
+// Forward progress: workgroups are dispatched in index order on each XCD and a
+// shrink workgroup never waits, so every shrink a waiting expand workgroup depends
+// on has been dispatched before it and finishes. Every wait is bounded anyway:
+// past kSpinLimit sleeps the workgroup records the epoch in the error word and
+// goes on, so no wave can spin forever.
+//
+// Every page load issues unconditionally: rows past the rank, invalid page ids and
+// lanes past the end of a row are pointed at 16-byte fill vectors (zero or NaN)
+// instead of being predicated, so no load waits on another load's result.
 #include "device_common.h"
 
 namespace slora {
@@ -23,215 +49,306 @@ namespace {
 
 using namespace dev;
 
-constexpr int kShrinkWaves = kMbShrinkRows / 2;  // 2 rows per wave
+constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 2;
-constexpr int kShrinkU = 8;                      // 16-byte vectors per lane per row in flight
-constexpr int kExpandWaves = kMbExpandCols / 512;
-constexpr int kExpandKU = 8;                     // B rows in flight per lane
+static_assert(kWaves * kRowsPerWave == kMbShrinkRows, "shrink row block");
+constexpr int kBatchVecs = 512;  // 16-byte vectors of a row per shrink batch (4096 elements)
+constexpr int kSlices = kBatchVecs / 64;
+constexpr int kKU = kMbRowsPerWave;
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kRedBytes = (kWaves - 1) * kMbExpandTok * 8 * 64 * 4;  // expand partial sums
 
-template <int DT, bool kUniformChunk>
-__global__ __launch_bounds__(64 * kShrinkWaves) void mbgmv_shrink_kernel(
-    Geom g, const int32_t* __restrict__ tok, const GroupDesc* __restrict__ groups,
-    const Item* __restrict__ items, const uint16_t* __restrict__ x, float* __restrict__ v) {
-  constexpr int G = kMbGroup, R = kRowsPerWave, U = kShrinkU;
-  const Item it = items[blockIdx.x];
-  const GroupDesc gd = groups[it.group];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int k0 = it.block * kMbShrinkRows + wave * R;
-  if (k0 >= gd.rank) return;  // wave-uniform; no barrier in this kernel
-  const int nrow = min(R, gd.rank - k0);
-  const int n = gd.n_tok;
-  const int nvec = g.d_in >> 3;  // 16-byte vectors per row
+__device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ int pick4(const int (&t)[kMbGroup], int i) {
+  return i == 0 ? t[0] : i == 1 ? t[1] : i == 2 ? t[2] : t[3];
+}
 
-  const uint16_t* xr[G];
+// ------------------------------------------------------------------ shrink role
+template <int DT, bool kUniformChunk, int G>
+__device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
+                                            const uint16_t* __restrict__ x, float* __restrict__ v,
+                                            uint4* xs) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int k0 = it.part * kMbShrinkRows + wave * kRowsPerWave;
+  const int nrow = max(0, min(kRowsPerWave, it.rank - k0));  // 0: this wave only stages x
+  const int n = it.n_tok;
+  const int nvec = g.d_in >> 3;
+  const int npid = nrow * g.cA;  // <= 2 * 32 (the planner limits cA)
+  const int my_pid = lane < npid ? g.pt[(int64_t)it.pt_base + (int64_t)k0 * g.cA + lane] : -1;
+  const int tok[kMbGroup] = {it.tok[0], it.tok[1], it.tok[2], it.tok[3]};
+
+  float acc[kRowsPerWave][G];
 #pragma unroll
-  for (int t = 0; t < G; ++t)
-    xr[t] = x + (int64_t)tok[gd.tok_begin + min(t, n - 1)] * g.d_in;
-
-  float acc[R][G];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < kRowsPerWave; ++r)
 #pragma unroll
     for (int t = 0; t < G; ++t) acc[r][t] = 0.f;
 
-  const int32_t* ptA = g.pt + gd.pt_base + (int64_t)k0 * g.cA;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  const uint32_t nw = nan2<DT>();
-  const uint4 nanv = make_uint4(nw, nw, nw, nw);
-
-  for (int vb = 0; vb < nvec; vb += 64 * U) {
-    uint4 a[R][U];
+  for (int vb = 0; vb < nvec; vb += kBatchVecs) {
+    uint4 a[kRowsPerWave][kSlices];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = vb + u * 64 + lane;
-      const int j = q * 8;
+    for (int u = 0; u < kSlices; ++u) {
+      const int qb = vb + u * 64;  // first vector of this slice (uniform)
+      const int q = min(qb + lane, nvec - 1);
       int c;
-      if constexpr (kUniformChunk) c = ((vb + u * 64) * 8) / g.P;  // the 512 elements share a page
-      else c = j / g.P;
-      const int off = j - c * g.P;
+      if constexpr (kUniformChunk) c = (qb * 8) / g.P;  // a 512-element slice never crosses a page
+      else c = (q * 8) / g.P;
+      const int off = q * 8 - c * g.P;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        a[r][u] = zero;
-        if (r < nrow && q < nvec) {
-          const int32_t page = ptA[r * g.cA + c];
-          a[r][u] = ((uint32_t)page < (uint64_t)g.n_pages)
-                        ? ld16(g.pool + (int64_t)page * g.P + off)
-                        : nanv;
-        }
+      for (int r = 0; r < kRowsPerWave; ++r) {
+        const bool live = qb < nvec && r < nrow;  // uniform
+        const int idx = live ? r * g.cA + c : 0;
+        int page;
+        if constexpr (kUniformChunk) page = readlane(my_pid, idx);
+        else page = __shfl(my_pid, idx);
+        const bool ok = (uint32_t)page < (uint64_t)g.n_pages;
+        a[r][u] = ld16(!live ? fill_zero() : ok ? g.pool + (int64_t)page * g.P + off : fill_nan<DT>());
       }
     }
+    // this batch of every token's x, global -> LDS directly; zero past the row end
 #pragma unroll
     for (int t = 0; t < G; ++t) {
-      if (t < n) {
+      const uint16_t* xr = x + (int64_t)tok[t < n ? t : 0] * g.d_in;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int q = vb + u * 64 + lane;
-          if (q < nvec) {
-            const uint4 xv = ld16(xr[t] + q * 8);
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[r][t] = dot8<DT>(a[r][u], xv, acc[r][t]);
-          }
-        }
+      for (int h = 0; h < 2; ++h) {
+        const int q = vb + h * 256 + tid;
+        __builtin_amdgcn_global_load_lds((t < n && q < nvec) ? xr + q * 8 : fill_zero(),
+                                         xs + t * kBatchVecs + h * 256 + wave * 64, 16, 0, 0);
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < G; ++t)
+#pragma unroll
+      for (int u = 0; u < kSlices; ++u) {
+        const uint4 xq = xs[t * kBatchVecs + u * 64 + lane];  // zero past the end of the row
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) acc[r][t] = dot8<DT>(a[r][u], xq, acc[r][t]);
+      }
+    __syncthreads();  // xs is overwritten by the next batch
   }
 
-  float flat[R * G];
+  constexpr int V = kRowsPerWave * G;
+  float flat[V];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < kRowsPerWave; ++r)
 #pragma unroll
     for (int t = 0; t < G; ++t) flat[r * G + t] = acc[r][t];
-  const float tot = xreduce<R * G>(flat, lane);
-  if (reduce_writer<R * G>(lane)) {
-    const int idx = reduce_index<R * G>(lane);
+  float tot[WaveSum<V>::kOut];
+  wave_sum<V>(flat, tot);
+#pragma unroll
+  for (int i = 0; i < WaveSum<V>::kOut; ++i) {
+    const int idx = wave_sum_index<V>(lane, i);
     const int r = idx / G, t = idx % G;
-    if (r < nrow && t < n)
-      v[(int64_t)tok[gd.tok_begin + t] * g.r_max + k0 + r] = tot;
+    if (wave_sum_writer<V>(lane, i) && r < nrow && t < n)
+      __hip_atomic_store(v + (int64_t)pick4(tok, t) * g.r_max + k0 + r, tot[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-template <int DT, bool kUniformChunk>
-__global__ __launch_bounds__(64 * kExpandWaves) void mbgmv_expand_kernel(
-    Geom g, const int32_t* __restrict__ tok, const GroupDesc* __restrict__ groups,
-    const float* __restrict__ v, uint16_t* __restrict__ y) {
-  constexpr int G = kMbGroup, KU = kExpandKU;
-  const GroupDesc gd = groups[blockIdx.x];
-  const int r = gd.rank, n = gd.n_tok;
-  __shared__ float vs[G][kMaxRank];
-  for (int i = threadIdx.x; i < n * r; i += 64 * kExpandWaves) {
-    const int t = i / r, k = i - t * r;
-    vs[t][k] = v[(int64_t)tok[gd.tok_begin + t] * g.r_max + k];
+// Advance the group's counter to (epoch << 16) | (count + 1). At most `need`
+// workgroups contend, so the bounded retry loop always succeeds well within it.
+__device__ __forceinline__ void publish(unsigned long long* c, unsigned long long epoch) {
+  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < 64; ++i) {
+    const unsigned long long want = (old >> 16) == epoch ? old + 1 : ((epoch << 16) | 1ull);
+    if (__hip_atomic_compare_exchange_strong(c, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      break;
   }
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int colw = (blockIdx.y * kExpandWaves + wave) * 512;
-  if (colw >= g.d_out) return;  // wave-uniform, after the only barrier
-  const int col = colw + lane * 8;
-  const bool valid = col < g.d_out;
+}
+
+// ------------------------------------------------------------------ expand role
+template <int DT, bool kUniformChunk, int NT>
+__device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
+                                            const float* __restrict__ v, uint16_t* __restrict__ y,
+                                            unsigned long long* counters, unsigned long long epoch,
+                                            unsigned long long* err, float* red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = it.rank, n = it.n_tok, split = it.split;
+  const int slices = kWaves / split, slice = wave / split, rp = wave % split;
+  const int rpw = (r + split - 1) / split;  // rows per wave (<= 32)
+  const int k_lo = min(r, rp * rpw), nk = min(r, k_lo + rpw) - k_lo;
+  const int colw = (it.part * slices + slice) * kMbWaveCols;  // first column of this wave
+  const bool wave_live = colw < g.d_out;
+  const int col = min(colw + lane * 8, g.d_out - 8);  // tail lanes duplicate a valid column
+  const bool lane_live = colw + lane * 8 < g.d_out;
   int c;
-  if constexpr (kUniformChunk) c = colw / g.P;
+  if constexpr (kUniformChunk) c = min(colw, g.d_out - 8) / g.P;
   else c = col / g.P;
   const int off = col - c * g.P;
-  const int32_t* ptB = g.pt + gd.pt_base + (int64_t)r * g.cA + c;
+  const int64_t pbase = (int64_t)it.pt_base + (int64_t)r * g.cA + c + (int64_t)k_lo * g.cB;
+  int pid = -1;  // lane k: page of this wave's row k_lo + k in its chunk (nk <= 32)
+  if constexpr (kUniformChunk) pid = lane < nk ? g.pt[pbase + (int64_t)lane * g.cB] : -1;
+  const int t0 = it.tok[0], t1 = it.tok[1];
 
-  float acc[G][8];
+  uint4 y0v[NT];
 #pragma unroll
-  for (int t = 0; t < G; ++t)
+  for (int t = 0; t < NT; ++t)
+    y0v[t] = ld16((rp == 0 && t < n && wave_live) ? y + (int64_t)(t ? t1 : t0) * g.d_out + col
+                                                   : fill_zero());
+
+  auto load_rows = [&](uint4 (&b)[kKU], int k) {
+#pragma unroll
+    for (int u = 0; u < kKU; ++u) {
+      const int kk = k + u;
+      const bool live = kk < nk && wave_live;  // uniform
+      int page;
+      if constexpr (kUniformChunk) page = readlane(pid, kk & 63);
+      else page = g.pt[live ? pbase + (int64_t)kk * g.cB : 0];
+      const bool ok = (uint32_t)page < (uint64_t)g.n_pages;
+      b[u] = ld16(!live ? fill_zero() : ok ? g.pool + (int64_t)page * g.P + off : fill_nan<DT>());
+    }
+  };
+
+  uint4 b[kKU];
+  load_rows(b, 0);
+
+  if (epoch) {  // the group's shrink items must have published v
+    if (tid == 0) {
+      const unsigned long long target = (epoch << 16) | (unsigned long long)it.need;
+      int spins = 0;
+      while (__hip_atomic_load(counters + it.group, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+             target) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kSpinLimit) {
+          __hip_atomic_store(err, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();  // v is read below with agent-scope loads, issued after the wait
+  }
+
+  float vr[NT];  // lane k: v[t][k_lo + k] (k < 32); rows 32..63 of a wave do not occur
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float* src = (t < n && lane < nk)
+                           ? v + (int64_t)(t ? t1 : t0) * g.r_max + k_lo + lane
+                           : reinterpret_cast<const float*>(fill_zero());
+    vr[t] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  float acc[NT][8];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
 
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  const uint32_t nw = nan2<DT>();
-  const uint4 nanv = make_uint4(nw, nw, nw, nw);
-  for (int k = 0; k < r; k += KU) {
-    uint4 b[KU];
+  auto mul_rows = [&](int k) {
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      b[u] = zero;
-      if (k + u < r && valid) {
-        const int32_t page = ptB[(int64_t)(k + u) * g.cB];
-        b[u] = ((uint32_t)page < (uint64_t)g.n_pages) ? ld16(g.pool + (int64_t)page * g.P + off)
-                                                       : nanv;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      if (k + u < r) {
+    for (int u = 0; u < kKU; ++u) {
+      if (k + u < nk) {  // uniform
         float bf[8];
         bf[0] = lo_f32<DT>(b[u].x); bf[1] = hi_f32<DT>(b[u].x);
         bf[2] = lo_f32<DT>(b[u].y); bf[3] = hi_f32<DT>(b[u].y);
         bf[4] = lo_f32<DT>(b[u].z); bf[5] = hi_f32<DT>(b[u].z);
         bf[6] = lo_f32<DT>(b[u].w); bf[7] = hi_f32<DT>(b[u].w);
 #pragma unroll
-        for (int t = 0; t < G; ++t) {
-          if (t < n) {
-            const float vt = vs[t][k + u];
+        for (int t = 0; t < NT; ++t) {
+          const float vt = readlane_f(vr[t], k + u);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(vt, bf[e], acc[t][e]);
-          }
+          for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(vt, bf[e], acc[t][e]);
         }
       }
     }
+  };
+  mul_rows(0);
+  if (nk > kKU) {  // rank > 64: a second batch of 16 rows (straight-line: no loop-carried copy)
+    load_rows(b, kKU);
+    mul_rows(kKU);
   }
-  if (!valid) return;
-  const float s = gd.scale;
+
+  if (split > 1) {  // the waves of a slice add their partial sums, in rank-part order
+    if (rp > 0) {
 #pragma unroll
-  for (int t = 0; t < G; ++t) {
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[(((wave - 1) * kMbExpandTok + t) * 8 + e) * 64 + lane] = acc[t][e];
+    }
+    __syncthreads();
+    if (rp == 0) {
+      for (int q = 1; q < split; ++q)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[t][e] += red[(((wave + q - 1) * kMbExpandTok + t) * 8 + e) * 64 + lane];
+    }
+  }
+  if (rp != 0 || !wave_live || !lane_live) return;
+  const float s = it.scale;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
     if (t < n) {
-      uint16_t* yr = y + (int64_t)tok[gd.tok_begin + t] * g.d_out + col;
-      const uint4 y0 = ld16(yr);
+      const uint4 y0 = y0v[t];
       uint4 o;
       o.x = pack2<DT>(fmaf(s, acc[t][0], lo_f32<DT>(y0.x)), fmaf(s, acc[t][1], hi_f32<DT>(y0.x)));
       o.y = pack2<DT>(fmaf(s, acc[t][2], lo_f32<DT>(y0.y)), fmaf(s, acc[t][3], hi_f32<DT>(y0.y)));
       o.z = pack2<DT>(fmaf(s, acc[t][4], lo_f32<DT>(y0.z)), fmaf(s, acc[t][5], hi_f32<DT>(y0.z)));
       o.w = pack2<DT>(fmaf(s, acc[t][6], lo_f32<DT>(y0.w)), fmaf(s, acc[t][7], hi_f32<DT>(y0.w)));
-      st16(yr, o);
+      st16(y + (int64_t)(t ? t1 : t0) * g.d_out + col, o);
     }
   }
 }
 
-template <int DT>
-hipError_t shrink_dt(const Geom& g, const int32_t* tok, const GroupDesc* groups, const Item* items,
-                     int32_t n_items, const void* x, float* v, hipStream_t s) {
-  const dim3 grid((unsigned)n_items), block(64 * kShrinkWaves);
-  if (g.P % 512 == 0)
-    hipLaunchKernelGGL((mbgmv_shrink_kernel<DT, true>), grid, block, 0, s, g, tok, groups, items,
-                       (const uint16_t*)x, v);
-  else
-    hipLaunchKernelGGL((mbgmv_shrink_kernel<DT, false>), grid, block, 0, s, g, tok, groups, items,
-                       (const uint16_t*)x, v);
-  return hipGetLastError();
+// items[0, n_shrink): shrink role; items[n_shrink, grid): expand role.
+template <int DT, bool kUniformChunk>
+__global__ __launch_bounds__(64 * kWaves) void mbgmv_kernel(
+    Geom g, const MbItem* __restrict__ items, int32_t n_shrink, const uint16_t* __restrict__ x,
+    float* __restrict__ v, uint16_t* __restrict__ y, unsigned long long* counters,
+    unsigned long long epoch, unsigned long long* err) {
+  extern __shared__ uint4 lds[];  // shrink: [G][kBatchVecs] of x; expand: partial sums
+  const MbItem it = items[blockIdx.x];
+  if (it.role == 0) {
+    const int n = it.n_tok;
+    static_assert(kMbGroup == 4, "shrink bodies cover 1, 2 and 4 tokens");
+    if (n <= 1) shrink_body<DT, kUniformChunk, 1>(g, it, x, v, lds);
+    else if (n <= 2) shrink_body<DT, kUniformChunk, 2>(g, it, x, v, lds);
+    else shrink_body<DT, kUniformChunk, 4>(g, it, x, v, lds);
+    if (epoch) {  // publish v for this group's expand items
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's agent-scope v stores have completed
+      __syncthreads();
+      if (threadIdx.x == 0) publish(counters + it.group, epoch);
+    }
+  } else {
+    float* red = reinterpret_cast<float*>(lds);
+    if (it.n_tok <= 1) expand_body<DT, kUniformChunk, 1>(g, it, v, y, counters, epoch, err, red);
+    else expand_body<DT, kUniformChunk, 2>(g, it, v, y, counters, epoch, err, red);
+  }
+  (void)n_shrink;
 }
 
 template <int DT>
-hipError_t expand_dt(const Geom& g, const int32_t* tok, const GroupDesc* groups, int32_t n_groups,
-                     const float* v, void* y, hipStream_t s) {
-  const dim3 grid((unsigned)n_groups, (unsigned)((g.d_out + kMbExpandCols - 1) / kMbExpandCols));
-  const dim3 block(64 * kExpandWaves);
+hipError_t launch_dt(const Geom& g, const MbItem* items, int32_t n_items, int32_t n_shrink,
+                     int32_t g_max, const void* x, float* v, void* y, unsigned long long* counters,
+                     unsigned long long epoch, unsigned long long* err, hipStream_t s) {
+  const dim3 grid((unsigned)n_items), block(64 * kWaves);
+  size_t lds = n_shrink > 0 ? (size_t)g_max * kBatchVecs * sizeof(uint4) : 0;
+  if (n_items > n_shrink) lds = lds > (size_t)kRedBytes ? lds : (size_t)kRedBytes;
   if (g.P % 512 == 0)
-    hipLaunchKernelGGL((mbgmv_expand_kernel<DT, true>), grid, block, 0, s, g, tok, groups, v,
-                       (uint16_t*)y);
+    hipLaunchKernelGGL((mbgmv_kernel<DT, true>), grid, block, lds, s, g, items, n_shrink,
+                       (const uint16_t*)x, v, (uint16_t*)y, counters, epoch, err);
   else
-    hipLaunchKernelGGL((mbgmv_expand_kernel<DT, false>), grid, block, 0, s, g, tok, groups, v,
-                       (uint16_t*)y);
+    hipLaunchKernelGGL((mbgmv_kernel<DT, false>), grid, block, lds, s, g, items, n_shrink,
+                       (const uint16_t*)x, v, (uint16_t*)y, counters, epoch, err);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mbgmv_shrink(const Geom& g, const int32_t* tok, const GroupDesc* groups,
-                               const Item* items, int32_t n_items, const void* x, float* v,
-                               hipStream_t s) {
+hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, int32_t n_shrink,
+                        int32_t max_tok, const void* x, float* v, void* y,
+                        unsigned long long* counters, unsigned long long epoch,
+                        unsigned long long* err, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
-  return g.dtype == SLORA_F16 ? shrink_dt<SLORA_F16>(g, tok, groups, items, n_items, x, v, s)
-                              : shrink_dt<SLORA_BF16>(g, tok, groups, items, n_items, x, v, s);
-}
-
-hipError_t launch_mbgmv_expand(const Geom& g, const int32_t* tok, const GroupDesc* groups,
-                               int32_t n_groups, const float* v, void* y, hipStream_t s) {
-  if (n_groups <= 0) return hipSuccess;
-  return g.dtype == SLORA_F16 ? expand_dt<SLORA_F16>(g, tok, groups, n_groups, v, y, s)
-                              : expand_dt<SLORA_BF16>(g, tok, groups, n_groups, v, y, s);
+  if (max_tok < 1 || max_tok > kMbGroup) return hipErrorInvalidValue;
+  const int g_max = max_tok <= 1 ? 1 : max_tok <= 2 ? 2 : 4;
+  return g.dtype == SLORA_F16
+             ? launch_dt<SLORA_F16>(g, items, n_items, n_shrink, g_max, x, v, y, counters, epoch, err, s)
+             : launch_dt<SLORA_BF16>(g, items, n_items, n_shrink, g_max, x, v, y, counters, epoch, err, s);
 }
 
 }  // namespace slora

@@ -6,15 +6,21 @@
 // S-LoRA overview, section "2. Heterogeneous Batching": adapters of different
 // ranks are batched together). The planner groups tokens that share an adapter so
 // that each group reads the adapter's pages once:
-//   * MBGMV groups: decode tokens bucketed by adapter (stable), split evenly into
-//     groups of at most kMbGroup tokens;
+//   * MBGMV groups: decode tokens bucketed by adapter (token order kept), split
+//     evenly into groups of at most kMbGroup tokens; each group becomes
+//     ceil(rank / 8) shrink items and, per pair of its tokens, one expand item per
+//     column tile;
 //   * SGMV tiles: a segment (or a bucket of ids) split evenly into tiles of at
 //     most kSgTile tokens.
 // Groups are ordered by descending rank so that the costliest work items are
 // dispatched first. The order only decides scheduling: every token's result is
 // computed by the same fixed sequence of operations wherever it lands.
+//
+// The plan is written straight into a pinned staging buffer that the kernels read
+// over the bus, so planning allocates nothing per call (scratch vectors are reused).
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 
 #include "internal.h"
 
@@ -24,34 +30,7 @@ namespace {
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-struct Pair {
-  int32_t adapter;
-  int32_t token;
-};
-
-// Append groups of at most `cap` tokens, sizes as even as possible, for one run
-// of tokens that share `adapter`.
-void split_run(const int32_t* toks, int32_t n, int32_t adapter, int32_t cap,
-               const slora_lora* L, std::vector<std::pair<GroupDesc, std::vector<int32_t>>>* out) {
-  if (n <= 0) return;
-  const int32_t g = (n + cap - 1) / cap;
-  const int32_t base = n / g, extra = n % g;
-  int32_t at = 0;
-  for (int32_t i = 0; i < g; ++i) {
-    const int32_t m = base + (i < extra ? 1 : 0);
-    GroupDesc d{};
-    d.n_tok = m;
-    d.pt_base = (int32_t)L->base[adapter];
-    d.rank = L->rank[adapter];
-    d.scale = L->scale[adapter];
-    out->emplace_back(d, std::vector<int32_t>(toks + at, toks + at + m));
-    at += m;
-  }
-}
-
-}  // namespace
-
-int validate_and_plan(const slora_lora* L, const slora_routing* R, Plan* plan) {
+int validate(const slora_lora* L, const slora_routing* R, int32_t* seg_end_out) {
   if (!L || !R) return fail(SLORA_E_INVALID, "lora / routing is NULL");
   if (!L->pool || (reinterpret_cast<uintptr_t>(L->pool) & 15))
     return fail(SLORA_E_INVALID, "lora.pool must be a 16-byte aligned device pointer");
@@ -69,6 +48,8 @@ int validate_and_plan(const slora_lora* L, const slora_routing* R, Plan* plan) {
   if (L->n_adapters < 0 || (L->n_adapters > 0 && (!L->base || !L->rank || !L->scale)))
     return fail(SLORA_E_INVALID, "lora.base / rank / scale missing");
   if (L->page_table_len < 0) return fail(SLORA_E_INVALID, "lora.page_table_len < 0");
+  if ((L->d_in + L->page_elems - 1) / L->page_elems > 32)  // a wave holds 2 rows' page ids
+    return fail(SLORA_E_INVALID, "d_in %d spans more than 32 pages of %d", L->d_in, L->page_elems);
   if (R->n_tokens < 0 || R->n_segments < 0)
     return fail(SLORA_E_INVALID, "routing.n_tokens / n_segments < 0");
   if (R->policy < SLORA_POLICY_AUTO || R->policy > SLORA_POLICY_SGMV)
@@ -88,135 +69,239 @@ int validate_and_plan(const slora_lora* L, const slora_routing* R, Plan* plan) {
   } else if (R->seg_offsets && R->seg_offsets[0] != 0) {
     return fail(SLORA_E_INVALID, "routing.seg_offsets[0] != 0");
   }
-  const int32_t n_dec = R->n_tokens - seg_end;
-  if (n_dec > 0 && !R->token_adapter) return fail(SLORA_E_INVALID, "routing.token_adapter is NULL");
+  if (R->n_tokens - seg_end > 0 && !R->token_adapter)
+    return fail(SLORA_E_INVALID, "routing.token_adapter is NULL");
+  *seg_end_out = seg_end;
+  return SLORA_OK;
+}
 
+// 1 if a token with adapter a does LoRA work, 0 if not, < 0 on an invalid id.
+int check_adapter(const slora_lora* L, int32_t a, int32_t cA, int32_t cB) {
+  if (a < -1 || a >= L->n_adapters)
+    return fail(SLORA_E_INVALID, "adapter id %d outside [-1, %d)", a, L->n_adapters);
+  if (a < 0) return 0;
+  const int32_t r = L->rank[a];
+  if (r < 0 || r > kMaxRank) return fail(SLORA_E_INVALID, "adapter %d rank %d invalid", a, r);
+  if (r == 0) return 0;
+  if (r > L->r_max) return fail(SLORA_E_INVALID, "adapter %d rank %d > r_max %d", a, r, L->r_max);
+  const int64_t b = L->base[a];
+  if (b < 0) return fail(SLORA_E_STATE, "adapter %d is not resident", a);
+  const int64_t end = b + (int64_t)r * (cA + cB);
+  if (end > L->page_table_len || end > INT32_MAX)
+    return fail(SLORA_E_INVALID, "adapter %d page-table entries [%lld, %lld) exceed length %lld", a,
+                (long long)b, (long long)end, (long long)L->page_table_len);
+  if (!L->page_table) return fail(SLORA_E_INVALID, "lora.page_table is NULL");
+  if (!std::isfinite(L->scale[a])) return fail(SLORA_E_INVALID, "adapter %d scale not finite", a);
+  return 1;
+}
+
+// Even split of n tokens into ceil(n / cap) parts: part i has base + (i < extra).
+struct Split {
+  int32_t parts, base, extra;
+  Split(int32_t n, int32_t cap) : parts((n + cap - 1) / cap), base(0), extra(0) {
+    if (parts) { base = n / parts; extra = n % parts; }
+  }
+  int32_t size(int32_t i) const { return base + (i < extra ? 1 : 0); }
+};
+
+int32_t n_ctile(const slora_lora* L, int32_t rank) {
+  const int32_t cols = 4 / mb_split(rank) * kMbWaveCols;
+  return (L->d_out + cols - 1) / cols;
+}
+
+}  // namespace
+
+int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc, PlanView* v) {
+  int32_t seg_end = 0;
+  int rc = validate(L, R, &seg_end);
+  if (rc) return rc;
   const int32_t P = L->page_elems;
   const int32_t cA = (L->d_in + P - 1) / P, cB = (L->d_out + P - 1) / P;
-
-  // Check one adapter id; returns 1 if the token does LoRA work, 0 if not, < 0 on error.
-  auto check = [&](int32_t a) -> int {
-    if (a < -1 || a >= L->n_adapters)
-      return fail(SLORA_E_INVALID, "adapter id %d outside [-1, %d)", a, L->n_adapters);
-    if (a < 0) return 0;
-    const int32_t r = L->rank[a];
-    if (r < 0 || r > kMaxRank) return fail(SLORA_E_INVALID, "adapter %d rank %d invalid", a, r);
-    if (r == 0) return 0;
-    if (r > L->r_max)
-      return fail(SLORA_E_INVALID, "adapter %d rank %d > r_max %d", a, r, L->r_max);
-    const int64_t b = L->base[a];
-    if (b < 0) return fail(SLORA_E_STATE, "adapter %d is not resident", a);
-    const int64_t end = b + (int64_t)r * (cA + cB);
-    if (end > L->page_table_len || end > INT32_MAX)
-      return fail(SLORA_E_INVALID, "adapter %d page-table entries [%lld, %lld) exceed length %lld", a,
-                  (long long)b, (long long)end, (long long)L->page_table_len);
-    if (!L->page_table) return fail(SLORA_E_INVALID, "lora.page_table is NULL");
-    if (!std::isfinite(L->scale[a])) return fail(SLORA_E_INVALID, "adapter %d scale not finite", a);
-    return 1;
-  };
-
-  std::vector<Pair> mb;  // tokens for MBGMV
-  std::vector<std::pair<GroupDesc, std::vector<int32_t>>> sg, mbg;
-  std::vector<Pair> sg_ids;  // per-token ids bucketed into SGMV tiles (policy SGMV)
+  sc->mb_keys.clear();
+  sc->sg_keys.clear();
+  sc->grp.clear();
+  sc->tiles.clear();
+  *v = PlanView{};
+  const int32_t S = R->n_segments;
   for (int32_t s = 0; s < S; ++s) {
-    const int32_t b = R->seg_offsets[s], e = R->seg_offsets[s + 1];
-    if (e == b) {
-      int rc = check(R->seg_adapter[s]);  // ids of empty segments must still be valid
-      if (rc < 0) return rc;
+    const int32_t b = R->seg_offsets[s], e = R->seg_offsets[s + 1], a = R->seg_adapter[s];
+    if (e == b) {  // an empty segment does no work; its id must still be in range
+      if (a < -1 || a >= L->n_adapters)
+        return fail(SLORA_E_INVALID, "adapter id %d outside [-1, %d)", a, L->n_adapters);
       continue;
     }
-    const int32_t a = R->seg_adapter[s];
-    int rc = check(a);
+    rc = check_adapter(L, a, cA, cB);
     if (rc < 0) return rc;
     if (rc == 0) continue;
     if (R->policy == SLORA_POLICY_MBGMV) {
-      for (int32_t t = b; t < e; ++t) mb.push_back({a, t});
-    } else {
-      std::vector<int32_t> toks((size_t)(e - b));
-      for (int32_t t = b; t < e; ++t) toks[(size_t)(t - b)] = t;
-      split_run(toks.data(), e - b, a, kSgTile, L, &sg);
+      for (int32_t t = b; t < e; ++t) sc->mb_keys.push_back(((uint64_t)a << 32) | (uint32_t)t);
+    } else {  // a segment's tokens are contiguous: tiles straight from the offsets
+      const Split sp(e - b, kSgTile);
+      int32_t at = b;
+      for (int32_t i = 0; i < sp.parts; ++i) {
+        sc->tiles.insert(sc->tiles.end(), {at, sp.size(i), a, 0});
+        at += sp.size(i);
+      }
     }
   }
+  const int32_t n_dec = R->n_tokens - seg_end;
   for (int32_t q = 0; q < n_dec; ++q) {
     const int32_t a = R->token_adapter[q];
-    int rc = check(a);
+    rc = check_adapter(L, a, cA, cB);
     if (rc < 0) return rc;
     if (rc == 0) continue;
-    if (R->policy == SLORA_POLICY_SGMV) sg_ids.push_back({a, seg_end + q});
-    else mb.push_back({a, seg_end + q});
+    const uint64_t key = ((uint64_t)a << 32) | (uint32_t)(seg_end + q);
+    (R->policy == SLORA_POLICY_SGMV ? sc->sg_keys : sc->mb_keys).push_back(key);
   }
-  auto by_adapter = [](const Pair& x, const Pair& y) { return x.adapter < y.adapter; };
-  std::stable_sort(mb.begin(), mb.end(), by_adapter);
-  std::stable_sort(sg_ids.begin(), sg_ids.end(), by_adapter);
-  auto bucket = [&](const std::vector<Pair>& v, int32_t cap,
-                    std::vector<std::pair<GroupDesc, std::vector<int32_t>>>* out) {
-    std::vector<int32_t> toks;
-    for (size_t i = 0; i < v.size();) {
+  // (adapter, token) keys sort adapter-major with tokens ascending: a stable bucket
+  std::sort(sc->mb_keys.begin(), sc->mb_keys.end());
+  std::sort(sc->sg_keys.begin(), sc->sg_keys.end());
+  auto runs = [](const std::vector<uint64_t>& keys, int32_t cap, std::vector<int32_t>* out,
+                 int32_t width) {
+    for (size_t i = 0; i < keys.size();) {
       size_t j = i;
-      toks.clear();
-      while (j < v.size() && v[j].adapter == v[i].adapter) toks.push_back(v[j++].token);
-      split_run(toks.data(), (int32_t)toks.size(), v[i].adapter, cap, L, out);
+      const uint32_t a = (uint32_t)(keys[i] >> 32);
+      while (j < keys.size() && (uint32_t)(keys[j] >> 32) == a) ++j;
+      const Split sp((int32_t)(j - i), cap);
+      int32_t at = (int32_t)i;
+      for (int32_t p = 0; p < sp.parts; ++p) {
+        out->push_back(at);
+        out->push_back(sp.size(p));
+        out->push_back((int32_t)a);
+        if (width == 4) out->push_back(1);  // tile whose tokens come from the keys
+        at += sp.size(p);
+      }
       i = j;
     }
   };
-  bucket(mb, kMbGroup, &mbg);
-  bucket(sg_ids, kSgTile, &sg);
+  runs(sc->mb_keys, kMbGroup, &sc->grp, 3);
+  runs(sc->sg_keys, kSgTile, &sc->tiles, 4);
 
-  auto by_rank_desc = [](const std::pair<GroupDesc, std::vector<int32_t>>& x,
-                         const std::pair<GroupDesc, std::vector<int32_t>>& y) {
-    return x.first.rank > y.first.rank;
+  // MBGMV groups by descending rank (stable)
+  const int32_t n_groups = (int32_t)(sc->grp.size() / 3);
+  sc->order.resize((size_t)n_groups);
+  for (int32_t gi = 0; gi < n_groups; ++gi) sc->order[(size_t)gi] = gi;
+  std::stable_sort(sc->order.begin(), sc->order.end(), [&](int32_t x, int32_t y) {
+    return L->rank[sc->grp[3 * (size_t)x + 2]] > L->rank[sc->grp[3 * (size_t)y + 2]];
+  });
+  // SGMV tiles by descending rank too (stable: segments first, then bucketed ids)
+  {
+    const size_t nt = sc->tiles.size() / 4;
+    std::vector<int32_t>& idx = sc->tile_order;
+    idx.resize(nt);
+    for (size_t i = 0; i < nt; ++i) idx[i] = (int32_t)i;
+    std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+      return L->rank[sc->tiles[4 * (size_t)x + 2]] > L->rank[sc->tiles[4 * (size_t)y + 2]];
+    });
+    sc->tiles_sorted.resize(sc->tiles.size());
+    for (size_t i = 0; i < nt; ++i)
+      for (int j = 0; j < 4; ++j) sc->tiles_sorted[4 * i + j] = sc->tiles[4 * (size_t)idx[i] + j];
+    sc->tiles.swap(sc->tiles_sorted);
+  }
+  int64_t n_shrink = 0, n_expand = 0;
+  int32_t max_tok = 0;
+  for (int32_t gi = 0; gi < n_groups; ++gi) {
+    const int32_t n = sc->grp[3 * (size_t)gi + 1], r = L->rank[sc->grp[3 * (size_t)gi + 2]];
+    n_shrink += (r + kMbShrinkRows - 1) / kMbShrinkRows;
+    n_expand += (int64_t)((n + kMbExpandTok - 1) / kMbExpandTok) * n_ctile(L, r);
+    max_tok = std::max(max_tok, n);
+  }
+  if (n_shrink + n_expand > INT32_MAX / 2) return fail(SLORA_E_INVALID, "batch too large");
+  v->n_mb = (int32_t)(n_shrink + n_expand);
+  v->n_mb_shrink = (int32_t)n_shrink;
+  v->n_groups = n_groups;
+  v->mb_max_tok = max_tok;
+  v->n_sg = (int32_t)(sc->tiles.size() / 4);
+  int32_t sg_tok = 0;
+  for (int32_t t = 0; t < v->n_sg; ++t) sg_tok += sc->tiles[4 * (size_t)t + 1];
+  v->n_tok = sg_tok;
+  v->n_routed = (int32_t)sc->mb_keys.size() + sg_tok;
+  return align_up((int64_t)v->n_mb * (int64_t)sizeof(MbItem), 64) +
+         align_up((int64_t)v->n_sg * (int64_t)sizeof(SgTile), 64) +
+         align_up((int64_t)sg_tok * 4, 64);
+}
+
+void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, void* buf,
+                PlanView* v) {
+  (void)R;
+  uint8_t* p = (uint8_t*)buf;
+  v->mb = (MbItem*)p;
+  p += align_up((int64_t)v->n_mb * (int64_t)sizeof(MbItem), 64);
+  v->sg = (SgTile*)p;
+  p += align_up((int64_t)v->n_sg * (int64_t)sizeof(SgTile), 64);
+  v->tok = (int32_t*)p;
+
+  auto base_item = [&](int32_t gi, int32_t slot) {
+    const int32_t k0 = sc->grp[3 * (size_t)gi], n = sc->grp[3 * (size_t)gi + 1];
+    const int32_t a = sc->grp[3 * (size_t)gi + 2];
+    MbItem it;
+    memset(&it, 0, sizeof it);
+    for (int32_t t = 0; t < n; ++t) it.tok[t] = (int32_t)(uint32_t)sc->mb_keys[(size_t)(k0 + t)];
+    it.n_tok = n;
+    it.pt_base = (int32_t)L->base[a];
+    it.rank = L->rank[a];
+    it.scale = L->scale[a];
+    it.group = slot;
+    return it;
   };
-  std::stable_sort(mbg.begin(), mbg.end(), by_rank_desc);
-  std::stable_sort(sg.begin(), sg.end(), by_rank_desc);
-
-  plan->tok.clear();
-  plan->mb_groups.clear();
-  plan->mb_shrink.clear();
-  plan->sg_tiles.clear();
-  for (auto& g : mbg) {
-    g.first.tok_begin = (int32_t)plan->tok.size();
-    plan->tok.insert(plan->tok.end(), g.second.begin(), g.second.end());
-    const int32_t gi = (int32_t)plan->mb_groups.size();
-    plan->mb_groups.push_back(g.first);
-    const int32_t nb = (g.first.rank + kMbShrinkRows - 1) / kMbShrinkRows;
-    for (int32_t blk = 0; blk < nb; ++blk) plan->mb_shrink.push_back({gi, blk});
+  MbItem* out = v->mb;
+  for (int32_t s = 0; s < v->n_groups; ++s) {  // shrink items, groups in dispatch order
+    const int32_t gi = sc->order[(size_t)s];
+    MbItem it = base_item(gi, s);
+    it.role = 0;
+    const int32_t nb = (it.rank + kMbShrinkRows - 1) / kMbShrinkRows;
+    for (int32_t b = 0; b < nb; ++b) {
+      it.part = b;
+      *out++ = it;
+    }
   }
-  for (auto& g : sg) {
-    g.first.tok_begin = (int32_t)plan->tok.size();
-    plan->tok.insert(plan->tok.end(), g.second.begin(), g.second.end());
-    plan->sg_tiles.push_back(g.first);
+  for (int32_t s = 0; s < v->n_groups; ++s) {  // expand items
+    const int32_t gi = sc->order[(size_t)s];
+    const MbItem g = base_item(gi, s);
+    const int32_t need = (g.rank + kMbShrinkRows - 1) / kMbShrinkRows, nct = n_ctile(L, g.rank);
+    for (int32_t t0 = 0; t0 < g.n_tok; t0 += kMbExpandTok) {
+      MbItem it = g;
+      it.n_tok = std::min(kMbExpandTok, g.n_tok - t0);
+      for (int32_t t = 0; t < kMbGroup; ++t) it.tok[t] = t < it.n_tok ? g.tok[t0 + t] : 0;
+      it.role = 1;
+      it.split = mb_split(g.rank);
+      it.need = need;
+      for (int32_t ct = 0; ct < nct; ++ct) {
+        it.part = ct;
+        *out++ = it;
+      }
+    }
   }
-  plan->n_routed = (int32_t)plan->tok.size();
-  return SLORA_OK;
+  int32_t at = 0;
+  for (int32_t t = 0; t < v->n_sg; ++t) {
+    const int32_t first = sc->tiles[4 * (size_t)t], n = sc->tiles[4 * (size_t)t + 1];
+    const int32_t a = sc->tiles[4 * (size_t)t + 2], from_keys = sc->tiles[4 * (size_t)t + 3];
+    SgTile tile;
+    memset(&tile, 0, sizeof tile);
+    tile.tok_begin = at;
+    tile.n_tok = n;
+    tile.pt_base = (int32_t)L->base[a];
+    tile.rank = L->rank[a];
+    tile.scale = L->scale[a];
+    v->sg[t] = tile;
+    for (int32_t q = 0; q < n; ++q)
+      v->tok[at + q] = from_keys ? (int32_t)(uint32_t)sc->sg_keys[(size_t)(first + q)] : first + q;
+    at += n;
+  }
 }
 
 int64_t workspace_bound(const slora_lora* L, const slora_routing* R) {
   const int64_t T = std::max<int32_t>(R->n_tokens, 0);
   const int64_t rm = std::max<int32_t>(L->r_max, 0);
-  int64_t b = align_up(T * rm * 4, 256);                                     // v
-  b += align_up(T * 4, 256);                                                 // tokens
-  b += align_up(T * (int64_t)sizeof(GroupDesc), 256);                        // MBGMV groups
-  b += align_up(T * ((rm + kMbShrinkRows - 1) / kMbShrinkRows) * (int64_t)sizeof(Item), 256);
-  b += align_up(T * (int64_t)sizeof(GroupDesc), 256);                        // SGMV tiles
-  return std::max<int64_t>(b, 256);
+  return kHeaderBytes + align_up(T * 8, 256) + align_up(T * rm * 4, 256);
 }
 
-PlanLayout layout_plan(const slora_lora* L, const slora_routing* R, const Plan& p) {
-  PlanLayout o{};
-  o.v_off = 0;
-  o.v_bytes = align_up((int64_t)std::max<int32_t>(R->n_tokens, 0) * std::max<int32_t>(L->r_max, 0) * 4, 256);
-  int64_t at = o.v_bytes;
-  o.blob_off = at;
-  o.tok_off = at;
-  at += align_up((int64_t)p.tok.size() * 4, 256);
-  o.mbg_off = at;
-  at += align_up((int64_t)p.mb_groups.size() * (int64_t)sizeof(GroupDesc), 256);
-  o.mbs_off = at;
-  at += align_up((int64_t)p.mb_shrink.size() * (int64_t)sizeof(Item), 256);
-  o.sgt_off = at;
-  at += align_up((int64_t)p.sg_tiles.size() * (int64_t)sizeof(GroupDesc), 256);
-  o.blob_bytes = at - o.blob_off;
-  o.total = std::max<int64_t>(at, 256);
+WsLayout ws_layout(const slora_lora* L, const slora_routing* R, int32_t n_groups) {
+  WsLayout o{};
+  o.cnt_off = kHeaderBytes;
+  const int64_t T = std::max<int32_t>(R->n_tokens, 0);
+  o.v_off = kHeaderBytes + align_up(std::max<int64_t>(T, n_groups) * 8, 256);
+  o.total = o.v_off + align_up(T * std::max<int32_t>(L->r_max, 0) * 4, 256);
   return o;
 }
 

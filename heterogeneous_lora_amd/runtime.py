@@ -54,7 +54,8 @@ class PagedLoRA:
     """One workload on one GPU: pool, resident adapters, page tables, inputs, workspace."""
 
     def __init__(self, wl, device: str = "cuda", adapters: Optional[List[int]] = None,
-                 fill_kv: bool = True, sentinel: bool = True, pool_seed: Optional[int] = None):
+                 fill_kv: bool = True, sentinel: bool = True, pool_seed: Optional[int] = None,
+                 store: Optional[HostStore] = None):
         self.wl = wl
         self.device = torch.device(device)
         P = wl.page_elems
@@ -71,8 +72,8 @@ class PagedLoRA:
         self.kv_pages = np.zeros(0, np.int32)
         if fill_kv:
             self._fill_kv()
-        self.store = HostStore(wl, self.adapters)
-        self.fetch()
+        self.store = store if store is not None else HostStore(wl, self.adapters)
+        self.fetch_ms = self.fetch()
         self.pt_dev, self.pt_len, self.base, self.rank = [], [], [], []
         for p in range(len(wl.projections)):
             pt, base, rank = self.pool.page_table(p, wl.n_adapters)
@@ -99,12 +100,15 @@ class PagedLoRA:
             got.append(self.pool.alloc_kv(free))
         self.kv_pages = np.concatenate(got) if got else np.zeros(0, np.int32)
 
-    def fetch(self, adapters: Optional[List[int]] = None):
-        """Fetch adapters on a side stream; the current stream waits for the done event."""
+    def fetch(self, adapters: Optional[List[int]] = None) -> float:
+        """Fetch adapters on a side stream; the current stream waits for the done event.
+        Returns the fetch time in ms (events on the side stream; waits for it)."""
         side = torch.cuda.Stream(device=self.device)
-        done = torch.cuda.Event()
-        done.record(side)  # creates the event so its handle can be passed down
+        done = torch.cuda.Event(enable_timing=True)
+        start = torch.cuda.Event(enable_timing=True)
         side.wait_stream(torch.cuda.current_stream(self.device))
+        start.record(side)
+        done.record(side)  # creates the event so its handle can be passed down
         n_proj = len(self.wl.projections)
         todo = self.adapters if adapters is None else adapters
         for i, a in enumerate(todo):
@@ -113,6 +117,8 @@ class PagedLoRA:
             self.pool.fetch_async(a, at, b, side.cuda_stream, done.cuda_event if last else None)
         torch.cuda.current_stream(self.device).wait_event(done)
         self._fetch_done = done
+        done.synchronize()
+        return start.elapsed_time(done)
 
     def call(self, proj: int, policy: int = _lib.POLICY_AUTO, wl=None) -> _lib.Call:
         wl = wl or self.wl
@@ -131,7 +137,8 @@ class PagedLoRA:
         return _dev_i16(self.wl.x(proj), self.device), _dev_i16(self.wl.y0(proj), self.device)
 
     def workspace(self, call: _lib.Call) -> torch.Tensor:
-        return torch.empty(_lib.workspace_size(call), dtype=torch.uint8, device=self.device)
+        """Device workspace for calls like `call` (zero-filled once, as the library requires)."""
+        return torch.zeros(_lib.workspace_size(call), dtype=torch.uint8, device=self.device)
 
     def apply(self, call: _lib.Call, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
               stream: Optional[torch.cuda.Stream] = None):

@@ -167,7 +167,11 @@ typedef struct {
   int32_t policy;               /* SLORA_POLICY_* */
 } slora_routing;
 
-/* Device workspace bytes a compute call with these arguments needs (>= 256). */
+/* Device workspace bytes a compute call with these arguments needs (>= 256). The
+ * workspace must be zero-filled once when it is allocated and then left to the
+ * library: it holds per-group completion counters tagged with a call epoch, which
+ * need no reset between calls. Calls that share a workspace must be ordered (one
+ * stream, or synchronized streams); calls on different workspaces may overlap. */
 int slora_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes);
 
 /* Shrink only: v[t, k] (fp32, DEVICE [n_tokens x r_max]) for routed tokens and
@@ -181,9 +185,37 @@ int slora_shrink(const slora_lora* lora, const slora_routing* routing, const voi
 int slora_expand(const slora_lora* lora, const slora_routing* routing, const float* v, void* y,
                  void* ws, int64_t ws_bytes, void* stream);
 
-/* Shrink + expand in one call (v lives in the workspace). y holds y0 on entry. */
+/* Shrink + expand in one call (v lives in the workspace). y holds y0 on entry.
+ * Decode tokens run in one launch: shrink workgroups publish v per group and the
+ * group's expand workgroups wait for it (a bounded wait; see
+ * slora_workspace_status). The work list is read by the kernels from a pinned
+ * host staging ring owned by the library. */
 int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
                 void* ws, int64_t ws_bytes, void* stream);
+
+/* Status of the last slora_apply that used workspace ws, once the work on
+ * `stream` has finished (this call synchronizes the stream): 0 = clean; 1 = a
+ * decode workgroup gave up waiting for v that another workgroup of the same
+ * launch should have published (that call's results are not valid). */
+int slora_workspace_status(const void* ws, void* stream, int32_t* status);
+
+/* Kernel timing for benchmarks. While enabled (on != 0), every kernel a compute
+ * call launches is bracketed by two HIP events recorded on the call's stream.
+ * Enabling clears the counters. Kernel ids: SLORA_K_MBGMV_SHRINK,
+ * SLORA_K_MBGMV_EXPAND, SLORA_K_SGMV_SHRINK, SLORA_K_SGMV_EXPAND, SLORA_K_MBGMV_FUSED (the decode
+ * shrink and expand in one launch, as slora_apply runs them). */
+#define SLORA_K_MBGMV_SHRINK 0
+#define SLORA_K_MBGMV_EXPAND 1
+#define SLORA_K_SGMV_SHRINK 2
+#define SLORA_K_SGMV_EXPAND 3
+#define SLORA_K_MBGMV_FUSED 4
+#define SLORA_K_COUNT 5
+int slora_timing_enable(int32_t on);
+
+/* Waits for the recorded events, then writes per kernel id the number of timed
+ * launches and their summed duration in milliseconds (arrays of n_kernels entries,
+ * n_kernels <= SLORA_K_COUNT), and clears the counters. */
+int slora_timing_read(int32_t n_kernels, int64_t* launches, double* total_ms);
 
 /* Work lists a call with these arguments would run, for inspection and tests
  * (host only; validates exactly like slora_apply, launches nothing). Groups come

@@ -36,6 +36,7 @@ def _run(rt, wl, proj=0, policy=0, mode="apply", inst=None, x=None, y0=None):
     if mode == "apply":
         inst.apply(call, xd, yd, ws)
         torch.cuda.synchronize()
+        assert _lib.workspace_status(ws.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
         return yd.cpu().numpy().view(np.uint16), inst
     v = torch.zeros(wl.n_tokens, inst.r_max, dtype=torch.float32, device="cuda")
     inst.shrink(call, xd, v, ws)

@@ -180,7 +180,7 @@ def test_validation_rejects_bad_calls():
 
 # ------------------------------------------------------------------ planner vs Python model
 
-MB_GROUP, SG_TILE = 8, 64
+MB_GROUP, SG_TILE = 4, 64
 
 
 def _even_split(toks, cap):
