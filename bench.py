@@ -218,7 +218,7 @@ def main():
     if sgmv_like:
         roofline["mfma_frac"] = round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
     kern_total_s = sum(ms for n, ms in timing.values()) * 1e-3 / args.steps
-    step_bytes = sum(sum(v["bytes"] for v in a.values()) for a in alg)
+    step_bytes = sum(kv["algorithmic_bytes"] * kv["launches"] for kv in kernels.values()) / args.steps
     log(f"[bench] kernels: {json.dumps(kernels)}")
     log(f"[bench] all kernels of a step: {kern_total_s * 1e6:.1f} us, "
         f"{step_bytes / kern_total_s / 1e9:.0f} GB/s algorithmic")

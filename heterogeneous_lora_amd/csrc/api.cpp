@@ -33,8 +33,7 @@ struct Ring {
 };
 std::mutex g_mu;  // guards the rings, the epoch map and the timing state
 std::map<int, Ring> g_rings;                 // per device
-std::map<const void*, uint64_t> g_ws_epoch;  // last epoch a fused call used per workspace
-std::atomic<uint64_t> g_epoch{0};
+std::map<const void*, uint32_t> g_ws_tag;  // last tag a fused call used, per workspace
 thread_local PlanScratch t_scratch;
 
 int acquire_slot(size_t n, StagingSlot** out) {
@@ -118,7 +117,7 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
     return fail(SLORA_E_INVALID, "v must be a 16-byte aligned device pointer");
   if (mode == kExpand && (!v_in || misaligned(v_in, 16)))
     return fail(SLORA_E_INVALID, "v must be a 16-byte aligned device pointer");
-  const WsLayout lay = ws_layout(L, R, pv.n_groups);
+  const WsLayout lay = ws_layout(L, R);
   if (!ws || misaligned(ws, 256)) return fail(SLORA_E_INVALID, "ws must be 256-byte aligned");
   if (ws_bytes < lay.total)
     return fail(SLORA_E_INVALID, "workspace of %lld bytes is smaller than the %lld needed",
@@ -144,11 +143,22 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
   g.cB = (L->d_out + g.P - 1) / g.P;
   g.pt = L->page_table;
   g.r_max = L->r_max;
-  unsigned long long* counters = (unsigned long long*)(wsb + lay.cnt_off);
   unsigned long long* err = (unsigned long long*)wsb;
   float* v = mode == kApply ? (float*)(wsb + lay.v_off) : (mode == kShrink ? v_out : nullptr);
   const float* vr = mode == kApply ? v : v_in;
   hipError_t e = hipSuccess;
+  uint32_t tag = 0;
+  if (mode == kApply && pv.n_mb) {
+    // A fresh tag per fused call on this workspace; before a tag could repeat,
+    // the whole workspace is cleared so no stale word can carry it.
+    uint32_t& last = g_ws_tag[ws];
+    if (last == 0xFFFFFFFFu) {
+      e = launch_zero(ws, ws_bytes & ~(int64_t)255, s);
+      if (e != hipSuccess) return hip_fail(e, "workspace clear");
+      last = 0;
+    }
+    tag = ++last;
+  }
   if (pv.n_sg && (mode & kShrink)) {
     e = timed_launch(SLORA_K_SGMV_SHRINK, s, [&] { return launch_sgmv_shrink(g, pv.tok, pv.sg, pv.n_sg, x, v, s); });
     if (e != hipSuccess) return hip_fail(e, "sgmv_shrink launch");
@@ -158,22 +168,21 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
     if (e != hipSuccess) return hip_fail(e, "sgmv_expand launch");
   }
   if (pv.n_mb) {
+    const bool has_expand = pv.n_mb > pv.n_mb_shrink;
     if (mode == kApply) {
-      const unsigned long long epoch = ++g_epoch;
-      g_ws_epoch[ws] = epoch;
       e = timed_launch(SLORA_K_MBGMV_FUSED, s, [&] {
-        return launch_mbgmv(g, pv.mb, pv.n_mb, pv.n_mb_shrink, pv.mb_max_tok, x, v, y, counters,
-                            epoch, err, s);
+        return launch_mbgmv(g, pv.mb, pv.n_mb, pv.n_mb_shrink > 0, has_expand, pv.mb_max_tok, x,
+                            v, y, tag, err, s);
       });
     } else if (mode == kShrink) {
       e = timed_launch(SLORA_K_MBGMV_SHRINK, s, [&] {
-        return launch_mbgmv(g, pv.mb, pv.n_mb_shrink, pv.n_mb_shrink, pv.mb_max_tok, x, v, nullptr,
-                            counters, 0, err, s);
+        return launch_mbgmv(g, pv.mb, pv.n_mb_shrink, true, false, pv.mb_max_tok, x, v, nullptr, 0,
+                            err, s);
       });
     } else {
       e = timed_launch(SLORA_K_MBGMV_EXPAND, s, [&] {
-        return launch_mbgmv(g, pv.mb + pv.n_mb_shrink, pv.n_mb - pv.n_mb_shrink, 0, pv.mb_max_tok,
-                            nullptr, const_cast<float*>(vr), y, counters, 0, err, s);
+        return launch_mbgmv(g, pv.mb + pv.n_mb_shrink, pv.n_mb - pv.n_mb_shrink, false, true,
+                            pv.mb_max_tok, nullptr, const_cast<float*>(vr), y, 0, err, s);
       });
     }
     if (e != hipSuccess) return hip_fail(e, "mbgmv launch");
@@ -222,7 +231,7 @@ int slora_timing_read(int32_t n_kernels, int64_t* launches, double* total_ms) {
 int slora_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes) {
   clear_error();
   if (!lora || !routing || !bytes) return fail(SLORA_E_INVALID, "workspace_size: NULL argument");
-  *bytes = workspace_bound(lora, routing);
+  *bytes = ws_layout(lora, routing).total;
   return SLORA_OK;
 }
 
@@ -234,8 +243,8 @@ int slora_workspace_status(const void* ws, void* stream, int32_t* status) {
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "workspace_status");
   std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_ws_epoch.find(ws);
-  *status = (it != g_ws_epoch.end() && flag == it->second) ? 1 : 0;
+  auto it = g_ws_tag.find(ws);
+  *status = (it != g_ws_tag.end() && it->second != 0 && flag == it->second) ? 1 : 0;
   return SLORA_OK;
 }
 

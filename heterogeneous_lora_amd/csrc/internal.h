@@ -40,9 +40,7 @@ struct MbItem {
   int32_t role;           // 0 = shrink, 1 = expand
   int32_t part;           // shrink: row block; expand: column tile
   int32_t split;          // expand: waves sharing a column slice (mb_split(rank))
-  int32_t group;          // completion counter slot of the item's group
-  int32_t need;           // expand: shrink items of the group
-  int32_t pad[3];
+  int32_t pad[5];
 };
 static_assert(sizeof(MbItem) == 64, "MbItem layout");
 
@@ -98,23 +96,23 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
                 PlanView* out);
 
 // Workspace (device, caller-owned, zero-filled once at allocation):
-//   [0, 256): header: uint64 epoch of the last failed wait
-//   [256, ...): uint64 completion counter per MBGMV group
-//   then v: float [n_tokens x r_max]
+//   [0, 256): header: uint64 tag of the last call whose wait gave up
+//   [256, ...): v as uint64 words [n_tokens x r_max]: (tag << 32) | fp32 bits
 constexpr int64_t kHeaderBytes = 256;
-int64_t workspace_bound(const slora_lora* L, const slora_routing* R);
 struct WsLayout {
-  int64_t cnt_off, v_off, total;
+  int64_t v_off, total;
 };
-WsLayout ws_layout(const slora_lora* L, const slora_routing* R, int32_t n_groups);
+WsLayout ws_layout(const slora_lora* L, const slora_routing* R);
 
 // ---------------------------------------------------------------- launchers
-// items[0, n_shrink) shrink, the rest expand. epoch != 0 makes the launch a fused
-// apply: shrink items publish their group's counter, expand items wait for it.
-hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, int32_t n_shrink,
-                        int32_t max_tok, const void* x, float* v, void* y,
-                        unsigned long long* counters, unsigned long long epoch,
-                        unsigned long long* err, hipStream_t s);
+// One launch over items (role per item; `shrinks` / `expands` say which roles
+// occur). tag != 0 makes it a fused apply: v is the workspace's tagged words,
+// shrink items write them and expand items poll them. tag == 0: v is plain fp32.
+hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
+                        bool expands, int32_t max_tok, const void* x, void* v, void* y,
+                        uint32_t tag, unsigned long long* err, hipStream_t s);
+// Zero `bytes` (a multiple of 16) of device memory with a kernel.
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s);
 hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, const void* x, float* v, hipStream_t s);
 hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* tiles,

@@ -14,30 +14,30 @@
 //     (global_load_lds_dwordx4); each wave loads its 2 rows (4096 elements per
 //     batch) with one 16-byte load per lane and slice, dots them with every
 //     token's x (v_dot2 fp16/bf16 -> fp32) and reduces all 2 x G lane partial
-//     sums at once (permlane swaps + DPP). v is stored with agent-scope stores;
-//     once they have completed, the workgroup advances the group's counter.
+//     sums at once (permlane swaps + DPP).
 //   expand items: (<= 2 tokens of a group, 2048 / split output columns). The 4
 //     waves cover 4 / split slices of 512 columns; the `split` waves of a slice
 //     share its rows (split = 1, 2, 4 for rank <= 16, <= 32, more), so no wave
 //     holds more than 16 B rows in flight and none walks a long chain of loads.
 //     Each wave loads its page ids, prefetches y0 and issues its B rows before it
-//     waits for the group's counter; then v arrives (agent-scope loads, lane k
-//     holds v[t][k]) and is read with v_readlane; acc[t][8] accumulates in fp32;
-//     the waves of a slice add their partial sums through LDS in a fixed order,
-//     and y = RNE(y0 + s * acc).
+//     needs v; lane k then holds v[t][k] and the rows read it with v_readlane;
+//     acc[t][8] accumulates in fp32; the waves of a slice add their partial sums
+//     through LDS in a fixed order, and y = RNE(y0 + s * acc).
 //
-// Memory ordering: v is written and read with relaxed agent-scope atomics (sc1:
-// performed at the agent coherence point); a writer waits for its stores to
-// complete (s_waitcnt) before the barrier that precedes the counter update, and
-// a reader issues its v loads only after it has observed the counter, so neither
-// side needs an L2 write-back or invalidation. Counters hold (epoch << 16) | count
-// and need no reset between calls (the workspace starts zeroed once).
+// Hand-off of v inside one launch: every v entry is one 64-bit word holding the
+// fp32 value and the 32-bit tag of the call that wrote it, stored by the shrink
+// item with a single relaxed agent-scope store (sc1: performed at the agent's
+// coherence point). An expand wave polls its own entries with agent-scope loads
+// until every one carries the call's tag. Value and tag travel in one word, so
+// no counters, fences or cache maintenance are needed and a shrink workgroup
+// exits as soon as its stores are issued. The host gives each call on a workspace
+// a fresh tag and clears the workspace before a tag could repeat.
 //
 // Forward progress: workgroups are dispatched in index order on each XCD and a
-// shrink workgroup never waits, so every shrink a waiting expand workgroup depends
-// on has been dispatched before it and finishes. Every wait is bounded anyway:
-// past kSpinLimit sleeps the workgroup records the epoch in the error word and
-// goes on, so no wave can spin forever.
+// shrink workgroup never waits, so every shrink an expand wave depends on has
+// been dispatched before it and finishes. Every wait is bounded anyway: past
+// kSpinLimit polls the wave records the tag in the error word and goes on, so no
+// wave can spin forever.
 //
 // Every page load issues unconditionally: rows past the rank, invalid page ids and
 // lanes past the end of a row are pointed at 16-byte fill vectors (zero or NaN)
@@ -67,10 +67,10 @@ __device__ __forceinline__ int pick4(const int (&t)[kMbGroup], int i) {
 }
 
 // ------------------------------------------------------------------ shrink role
-template <int DT, bool kUniformChunk, int G>
+template <int DT, bool kUniformChunk, int G, bool kTag>
 __device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
-                                            const uint16_t* __restrict__ x, float* __restrict__ v,
-                                            uint4* xs) {
+                                            const uint16_t* __restrict__ x, void* __restrict__ v,
+                                            uint32_t tag, uint4* xs) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int k0 = it.part * kMbShrinkRows + wave * kRowsPerWave;
   const int nrow = max(0, min(kRowsPerWave, it.rank - k0));  // 0: this wave only stages x
@@ -142,30 +142,23 @@ __device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
   for (int i = 0; i < WaveSum<V>::kOut; ++i) {
     const int idx = wave_sum_index<V>(lane, i);
     const int r = idx / G, t = idx % G;
-    if (wave_sum_writer<V>(lane, i) && r < nrow && t < n)
-      __hip_atomic_store(v + (int64_t)pick4(tok, t) * g.r_max + k0 + r, tot[i], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Advance the group's counter to (epoch << 16) | (count + 1). At most `need`
-// workgroups contend, so the bounded retry loop always succeeds well within it.
-__device__ __forceinline__ void publish(unsigned long long* c, unsigned long long epoch) {
-  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int i = 0; i < 64; ++i) {
-    const unsigned long long want = (old >> 16) == epoch ? old + 1 : ((epoch << 16) | 1ull);
-    if (__hip_atomic_compare_exchange_strong(c, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      break;
+    if (wave_sum_writer<V>(lane, i) && r < nrow && t < n) {
+      const int64_t at = (int64_t)pick4(tok, t) * g.r_max + k0 + r;
+      if constexpr (kTag)
+        __hip_atomic_store(static_cast<unsigned long long*>(v) + at,
+                           ((unsigned long long)tag << 32) | __float_as_uint(tot[i]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else
+        static_cast<float*>(v)[at] = tot[i];
+    }
   }
 }
 
 // ------------------------------------------------------------------ expand role
-template <int DT, bool kUniformChunk, int NT>
+template <int DT, bool kUniformChunk, int NT, bool kTag>
 __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
-                                            const float* __restrict__ v, uint16_t* __restrict__ y,
-                                            unsigned long long* counters, unsigned long long epoch,
-                                            unsigned long long* err, float* red) {
+                                            const void* __restrict__ v, uint16_t* __restrict__ y,
+                                            uint32_t tag, unsigned long long* err, float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = it.rank, n = it.n_tok, split = it.split;
   const int slices = kWaves / split, slice = wave / split, rp = wave % split;
@@ -206,29 +199,39 @@ __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
   uint4 b[kKU];
   load_rows(b, 0);
 
-  if (epoch) {  // the group's shrink items must have published v
-    if (tid == 0) {
-      const unsigned long long target = (epoch << 16) | (unsigned long long)it.need;
-      int spins = 0;
-      while (__hip_atomic_load(counters + it.group, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
-             target) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
-          __hip_atomic_store(err, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-    __syncthreads();  // v is read below with agent-scope loads, issued after the wait
-  }
-
   float vr[NT];  // lane k: v[t][k_lo + k] (k < 32); rows 32..63 of a wave do not occur
+  if constexpr (kTag) {
+    // poll until every entry this wave needs carries the call's tag
+    const unsigned long long* vt = static_cast<const unsigned long long*>(v);
+    const unsigned long long* src[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float* src = (t < n && lane < nk)
-                           ? v + (int64_t)(t ? t1 : t0) * g.r_max + k_lo + lane
-                           : reinterpret_cast<const float*>(fill_zero());
-    vr[t] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = 0; t < NT; ++t)
+      src[t] = (t < n && lane < nk) ? vt + (int64_t)(t ? t1 : t0) * g.r_max + k_lo + lane
+                                    : reinterpret_cast<const unsigned long long*>(fill_zero());
+    unsigned long long w[NT];
+    for (int spins = 0;; ++spins) {
+      bool ready = true;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        w[t] = __hip_atomic_load(src[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ready = ready && (!(t < n && lane < nk) || (uint32_t)(w[t] >> 32) == tag);
+      }
+      if (__all(ready)) break;
+      if (spins >= kSpinLimit) {
+        if (lane == 0) __hip_atomic_store(err, (unsigned long long)tag, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vr[t] = __uint_as_float((uint32_t)w[t]);
+  } else {
+    const float* vf = static_cast<const float*>(v);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      vr[t] = *((t < n && lane < nk) ? vf + (int64_t)(t ? t1 : t0) * g.r_max + k_lo + lane
+                                     : reinterpret_cast<const float*>(fill_zero()));
   }
 
   float acc[NT][8];
@@ -294,61 +297,71 @@ __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
   }
 }
 
-// items[0, n_shrink): shrink role; items[n_shrink, grid): expand role.
-template <int DT, bool kUniformChunk>
+// Role per item. kTag: one fused call (v tagged, expand waves poll for it);
+// otherwise a shrink-only or expand-only launch with plain fp32 v.
+template <int DT, bool kUniformChunk, bool kTag>
 __global__ __launch_bounds__(64 * kWaves) void mbgmv_kernel(
-    Geom g, const MbItem* __restrict__ items, int32_t n_shrink, const uint16_t* __restrict__ x,
-    float* __restrict__ v, uint16_t* __restrict__ y, unsigned long long* counters,
-    unsigned long long epoch, unsigned long long* err) {
+    Geom g, const MbItem* __restrict__ items, const uint16_t* __restrict__ x, void* v,
+    uint16_t* __restrict__ y, uint32_t tag, unsigned long long* err) {
   extern __shared__ uint4 lds[];  // shrink: [G][kBatchVecs] of x; expand: partial sums
   const MbItem it = items[blockIdx.x];
   if (it.role == 0) {
     const int n = it.n_tok;
     static_assert(kMbGroup == 4, "shrink bodies cover 1, 2 and 4 tokens");
-    if (n <= 1) shrink_body<DT, kUniformChunk, 1>(g, it, x, v, lds);
-    else if (n <= 2) shrink_body<DT, kUniformChunk, 2>(g, it, x, v, lds);
-    else shrink_body<DT, kUniformChunk, 4>(g, it, x, v, lds);
-    if (epoch) {  // publish v for this group's expand items
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's agent-scope v stores have completed
-      __syncthreads();
-      if (threadIdx.x == 0) publish(counters + it.group, epoch);
-    }
+    if (n <= 1) shrink_body<DT, kUniformChunk, 1, kTag>(g, it, x, v, tag, lds);
+    else if (n <= 2) shrink_body<DT, kUniformChunk, 2, kTag>(g, it, x, v, tag, lds);
+    else shrink_body<DT, kUniformChunk, 4, kTag>(g, it, x, v, tag, lds);
   } else {
     float* red = reinterpret_cast<float*>(lds);
-    if (it.n_tok <= 1) expand_body<DT, kUniformChunk, 1>(g, it, v, y, counters, epoch, err, red);
-    else expand_body<DT, kUniformChunk, 2>(g, it, v, y, counters, epoch, err, red);
+    if (it.n_tok <= 1) expand_body<DT, kUniformChunk, 1, kTag>(g, it, v, y, tag, err, red);
+    else expand_body<DT, kUniformChunk, 2, kTag>(g, it, v, y, tag, err, red);
   }
-  (void)n_shrink;
 }
 
-template <int DT>
-hipError_t launch_dt(const Geom& g, const MbItem* items, int32_t n_items, int32_t n_shrink,
-                     int32_t g_max, const void* x, float* v, void* y, unsigned long long* counters,
-                     unsigned long long epoch, unsigned long long* err, hipStream_t s) {
+template <int DT, bool kTag>
+hipError_t launch_dt(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
+                     bool expands, int32_t g_max, const void* x, void* v, void* y, uint32_t tag,
+                     unsigned long long* err, hipStream_t s) {
   const dim3 grid((unsigned)n_items), block(64 * kWaves);
-  size_t lds = n_shrink > 0 ? (size_t)g_max * kBatchVecs * sizeof(uint4) : 0;
-  if (n_items > n_shrink) lds = lds > (size_t)kRedBytes ? lds : (size_t)kRedBytes;
+  size_t lds = shrinks ? (size_t)g_max * kBatchVecs * sizeof(uint4) : 0;
+  if (expands) lds = lds > (size_t)kRedBytes ? lds : (size_t)kRedBytes;
   if (g.P % 512 == 0)
-    hipLaunchKernelGGL((mbgmv_kernel<DT, true>), grid, block, lds, s, g, items, n_shrink,
-                       (const uint16_t*)x, v, (uint16_t*)y, counters, epoch, err);
+    hipLaunchKernelGGL((mbgmv_kernel<DT, true, kTag>), grid, block, lds, s, g, items,
+                       (const uint16_t*)x, v, (uint16_t*)y, tag, err);
   else
-    hipLaunchKernelGGL((mbgmv_kernel<DT, false>), grid, block, lds, s, g, items, n_shrink,
-                       (const uint16_t*)x, v, (uint16_t*)y, counters, epoch, err);
+    hipLaunchKernelGGL((mbgmv_kernel<DT, false, kTag>), grid, block, lds, s, g, items,
+                       (const uint16_t*)x, v, (uint16_t*)y, tag, err);
   return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 }  // namespace
 
-hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, int32_t n_shrink,
-                        int32_t max_tok, const void* x, float* v, void* y,
-                        unsigned long long* counters, unsigned long long epoch,
-                        unsigned long long* err, hipStream_t s) {
+hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
+                        bool expands, int32_t max_tok, const void* x, void* v, void* y,
+                        uint32_t tag, unsigned long long* err, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   if (max_tok < 1 || max_tok > kMbGroup) return hipErrorInvalidValue;
   const int g_max = max_tok <= 1 ? 1 : max_tok <= 2 ? 2 : 4;
+  if (tag)
+    return g.dtype == SLORA_F16
+               ? launch_dt<SLORA_F16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, s)
+               : launch_dt<SLORA_BF16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, s);
   return g.dtype == SLORA_F16
-             ? launch_dt<SLORA_F16>(g, items, n_items, n_shrink, g_max, x, v, y, counters, epoch, err, s)
-             : launch_dt<SLORA_BF16>(g, items, n_items, n_shrink, g_max, x, v, y, counters, epoch, err, s);
+             ? launch_dt<SLORA_F16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, s)
+             : launch_dt<SLORA_BF16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, s);
+}
+
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s) {
+  if (bytes <= 0) return hipSuccess;
+  const int64_t n = bytes / 16;  // callers pass multiples of 256 bytes
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)p, n);
+  return hipGetLastError();
 }
 
 }  // namespace slora

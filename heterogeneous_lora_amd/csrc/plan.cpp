@@ -231,7 +231,7 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
   p += align_up((int64_t)v->n_sg * (int64_t)sizeof(SgTile), 64);
   v->tok = (int32_t*)p;
 
-  auto base_item = [&](int32_t gi, int32_t slot) {
+  auto base_item = [&](int32_t gi) {
     const int32_t k0 = sc->grp[3 * (size_t)gi], n = sc->grp[3 * (size_t)gi + 1];
     const int32_t a = sc->grp[3 * (size_t)gi + 2];
     MbItem it;
@@ -241,13 +241,12 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
     it.pt_base = (int32_t)L->base[a];
     it.rank = L->rank[a];
     it.scale = L->scale[a];
-    it.group = slot;
     return it;
   };
   MbItem* out = v->mb;
   for (int32_t s = 0; s < v->n_groups; ++s) {  // shrink items, groups in dispatch order
     const int32_t gi = sc->order[(size_t)s];
-    MbItem it = base_item(gi, s);
+    MbItem it = base_item(gi);
     it.role = 0;
     const int32_t nb = (it.rank + kMbShrinkRows - 1) / kMbShrinkRows;
     for (int32_t b = 0; b < nb; ++b) {
@@ -257,15 +256,14 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
   }
   for (int32_t s = 0; s < v->n_groups; ++s) {  // expand items
     const int32_t gi = sc->order[(size_t)s];
-    const MbItem g = base_item(gi, s);
-    const int32_t need = (g.rank + kMbShrinkRows - 1) / kMbShrinkRows, nct = n_ctile(L, g.rank);
+    const MbItem g = base_item(gi);
+    const int32_t nct = n_ctile(L, g.rank);
     for (int32_t t0 = 0; t0 < g.n_tok; t0 += kMbExpandTok) {
       MbItem it = g;
       it.n_tok = std::min(kMbExpandTok, g.n_tok - t0);
       for (int32_t t = 0; t < kMbGroup; ++t) it.tok[t] = t < it.n_tok ? g.tok[t0 + t] : 0;
       it.role = 1;
       it.split = mb_split(g.rank);
-      it.need = need;
       for (int32_t ct = 0; ct < nct; ++ct) {
         it.part = ct;
         *out++ = it;
@@ -290,18 +288,11 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
   }
 }
 
-int64_t workspace_bound(const slora_lora* L, const slora_routing* R) {
-  const int64_t T = std::max<int32_t>(R->n_tokens, 0);
-  const int64_t rm = std::max<int32_t>(L->r_max, 0);
-  return kHeaderBytes + align_up(T * 8, 256) + align_up(T * rm * 4, 256);
-}
-
-WsLayout ws_layout(const slora_lora* L, const slora_routing* R, int32_t n_groups) {
+WsLayout ws_layout(const slora_lora* L, const slora_routing* R) {
   WsLayout o{};
-  o.cnt_off = kHeaderBytes;
   const int64_t T = std::max<int32_t>(R->n_tokens, 0);
-  o.v_off = kHeaderBytes + align_up(std::max<int64_t>(T, n_groups) * 8, 256);
-  o.total = o.v_off + align_up(T * std::max<int32_t>(L->r_max, 0) * 4, 256);
+  o.v_off = kHeaderBytes;
+  o.total = o.v_off + align_up(T * std::max<int32_t>(L->r_max, 0) * 8, 256);
   return o;
 }
 
