@@ -24,6 +24,14 @@ constexpr int kMbExpandTok = 2;     // MBGMV expand: tokens per workgroup
 constexpr int kMbWaveCols = 512;    // MBGMV expand: output columns per wave (64 lanes x 8)
 constexpr int kMbRowsPerWave = 16;  // MBGMV expand: B rows a wave keeps in flight
 constexpr int kSgTile = 64;         // SGMV: tokens per tile
+constexpr int kSgCols = 256;        // SGMV expand: output columns per workgroup
+constexpr int kSgMaxSplit = 8;      // SGMV shrink: most k-ranges d_in is cut into
+
+// k-ranges the SGMV shrink may cut d_in into (each at least 256 long).
+inline int sg_max_split(int d_in) {
+  const int s = d_in / 256;
+  return s < 1 ? 1 : s > kSgMaxSplit ? kSgMaxSplit : s;
+}
 
 // Expand waves that split one column slice's rows: 1, 2 or 4 (4 waves per workgroup).
 inline int mb_split(int rank) { return rank <= 16 ? 1 : rank <= 32 ? 2 : 4; }
@@ -51,7 +59,8 @@ struct SgTile {
   int32_t pt_base;
   int32_t rank;
   float scale;
-  int32_t pad[3];
+  int32_t first_tok;  // >= 0: the tokens are first_tok + [0, n_tok) (a segment); -1: the list
+  int32_t pad[2];
 };
 static_assert(sizeof(SgTile) == 32, "SgTile layout");
 
@@ -78,6 +87,7 @@ struct PlanView {
   int32_t n_tok = 0;
   int32_t n_routed = 0;
   int32_t mb_max_tok = 0;
+  int32_t sg_max_rank = 0;
 };
 
 // Scratch the planner reuses between calls (thread-local, grows only).
@@ -97,10 +107,11 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
 
 // Workspace (device, caller-owned, zero-filled once at allocation):
 //   [0, 256): header: uint64 tag of the last call whose wait gave up
-//   [256, ...): v as uint64 words [n_tokens x r_max]: (tag << 32) | fp32 bits
+//   v_off: MBGMV v as uint64 words [n_tokens x r_max]: (tag << 32) | fp32 bits
+//   sg_off: SGMV partial v, fp32 [sg_max_split(d_in)][n_tokens x r_max]
 constexpr int64_t kHeaderBytes = 256;
 struct WsLayout {
-  int64_t v_off, total;
+  int64_t v_off, sg_off, total;
 };
 WsLayout ws_layout(const slora_lora* L, const slora_routing* R);
 
@@ -113,10 +124,19 @@ hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, boo
                         uint32_t tag, unsigned long long* err, hipStream_t s);
 // Zero `bytes` (a multiple of 16) of device memory with a kernel.
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s);
+// SGMV shrink over ksplit k-ranges of kc (a multiple of 128) elements: range ks
+// writes its partial sums to vpart + ks * split_stride ([n_tokens x r_max] rows).
+// The expand adds the ksplit partials in range order.
+struct SgSplit {
+  int32_t ksplit, kc;
+};
+SgSplit sg_split(int32_t d_in, int32_t n_tiles);
 hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const SgTile* tiles,
-                              int32_t n_tiles, const void* x, float* v, hipStream_t s);
+                              int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
+                              const void* x, float* vpart, int64_t split_stride, hipStream_t s);
 hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* tiles,
-                              int32_t n_tiles, const float* v, void* y, hipStream_t s);
+                              int32_t n_tiles, int32_t max_rank, int32_t ksplit,
+                              const float* vpart, int64_t split_stride, void* y, hipStream_t s);
 
 constexpr int kFetchMaxPages = 240;
 struct FetchArgs {

@@ -281,7 +281,9 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
     tile.pt_base = (int32_t)L->base[a];
     tile.rank = L->rank[a];
     tile.scale = L->scale[a];
+    tile.first_tok = from_keys ? -1 : first;
     v->sg[t] = tile;
+    v->sg_max_rank = std::max(v->sg_max_rank, tile.rank);
     for (int32_t q = 0; q < n; ++q)
       v->tok[at + q] = from_keys ? (int32_t)(uint32_t)sc->sg_keys[(size_t)(first + q)] : first + q;
     at += n;
@@ -291,8 +293,10 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
 WsLayout ws_layout(const slora_lora* L, const slora_routing* R) {
   WsLayout o{};
   const int64_t T = std::max<int32_t>(R->n_tokens, 0);
+  const int64_t rows = T * std::max<int32_t>(L->r_max, 0);
   o.v_off = kHeaderBytes;
-  o.total = o.v_off + align_up(T * std::max<int32_t>(L->r_max, 0) * 8, 256);
+  o.sg_off = o.v_off + align_up(rows * 8, 256);
+  o.total = o.sg_off + align_up((int64_t)sg_max_split(std::max<int32_t>(L->d_in, 0)) * rows * 4, 256);
   return o;
 }
 

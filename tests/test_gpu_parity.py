@@ -58,8 +58,12 @@ SMALL = [
 ]
 
 
+POLICIES = [0, 1, 2]
+POLICY_IDS = ["auto", "mbgmv", "sgmv"]
+
+
 @pytest.mark.parametrize("kw", SMALL, ids=[f"s{k['seed']}" for k in SMALL])
-@pytest.mark.parametrize("policy", [1], ids=["mbgmv"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 def test_small_parity(rt, kw, policy):
     wl = workloads.random_small(**kw)
     say(f"[gpu] small parity {kw} policy={policy}")
@@ -69,10 +73,11 @@ def test_small_parity(rt, kw, policy):
     inst.close()
 
 
-def test_tiny_decode_parity(rt):
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
+def test_tiny_decode_parity(rt, policy):
     wl = workloads.tiny(0)
-    say("[gpu] tiny_decode parity")
-    y, inst = _run(rt, wl)
+    say(f"[gpu] tiny_decode parity policy={policy}")
+    y, inst = _run(rt, wl, policy=policy)
     ref, _ = oracle_ref(wl, 0)
     check_close(y, ref, wl.dtype, "tiny_decode")
     inst.close()
@@ -96,10 +101,20 @@ def test_decode7b_parity(rt, decode7b):
     say(f"[gpu] decode_7b max err / scale = {rel:.2e} (tol {TOL})")
 
 
-def test_decode7b_shrink_v(rt, decode7b):
+def test_decode7b_sgmv_parity(rt, decode7b):
+    """The same decode batch with every token forced onto SGMV tiles (adapter buckets)."""
     wl, inst = decode7b
-    say("[gpu] decode_7b shrink v parity")
-    v, _ = _run(rt, wl, inst=inst, mode="shrink")
+    say("[gpu] decode_7b parity through SGMV")
+    y, _ = _run(rt, wl, inst=inst, policy=2)
+    ref, _ = oracle_ref(wl, 0)
+    check_close(y, ref, wl.dtype, "decode_7b sgmv")
+
+
+@pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
+def test_decode7b_shrink_v(rt, decode7b, policy):
+    wl, inst = decode7b
+    say(f"[gpu] decode_7b shrink v parity policy={policy}")
+    v, _ = _run(rt, wl, inst=inst, mode="shrink", policy=policy)
     _, v_ref = oracle_ref(wl, 0, want_v=True)
     ids = wl.token_adapter
     for t in range(wl.n_tokens):
@@ -109,12 +124,13 @@ def test_decode7b_shrink_v(rt, decode7b):
         assert err <= TOL * scale, (t, err, scale)
 
 
-def test_decode7b_expand_only(rt, decode7b):
+@pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
+def test_decode7b_expand_only(rt, decode7b, policy):
     """slora_expand fed the oracle's v (as fp32) reproduces the oracle's y."""
     wl, inst = decode7b
-    say("[gpu] decode_7b expand-only parity")
+    say(f"[gpu] decode_7b expand-only parity policy={policy}")
     ref, v_ref = oracle_ref(wl, 0, want_v=True)
-    call = inst.call(0)
+    call = inst.call(0, policy)
     _, yd = inst.inputs(0)
     vt = torch.zeros(wl.n_tokens, inst.r_max, dtype=torch.float32)
     vt[:, :v_ref.shape[1]] = torch.from_numpy(v_ref.astype(np.float32))
@@ -144,26 +160,31 @@ def test_decode7b_batch_invariance(rt, decode7b):
     assert np.array_equal(yd.cpu().numpy().view(np.uint16), y_all[keep])
 
 
-def test_page_permutation_bit_identical(rt):
-    """Two pools with different shuffles (so every page sits elsewhere) give identical bits."""
-    wl = workloads.random_small(201, d_in=1024, d_out=1536, page_elems=512, n_tokens=40,
-                                n_segments=0, rank_choices=(8, 16, 32), n_pages=4096)
-    say("[gpu] page permutation")
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
+def test_page_permutation_bit_identical(rt, policy):
+    """Two pools with different shuffles (so every page sits elsewhere) give identical bits,
+    and a second call on the same inputs repeats the first bit for bit."""
+    wl = workloads.random_small(201, d_in=1024, d_out=1536, page_elems=512, n_tokens=150,
+                                n_segments=3, rank_choices=(8, 16, 32, 100), n_pages=8192)
+    say(f"[gpu] page permutation policy={policy}")
     a = rt.PagedLoRA(wl, pool_seed=1)
     b = rt.PagedLoRA(wl, pool_seed=2)
     assert not np.array_equal(a.pt_dev[0].cpu().numpy(), b.pt_dev[0].cpu().numpy())
-    ya, _ = _run(rt, wl, inst=a)
-    yb, _ = _run(rt, wl, inst=b)
+    ya, _ = _run(rt, wl, inst=a, policy=policy)
+    yb, _ = _run(rt, wl, inst=b, policy=policy)
+    ya2, _ = _run(rt, wl, inst=a, policy=policy)
     assert np.array_equal(ya, yb)
+    assert np.array_equal(ya, ya2)
     a.close()
     b.close()
 
 
-def test_idle_tokens_untouched(rt):
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
+def test_idle_tokens_untouched(rt, policy):
     wl = workloads.random_small(202, n_tokens=60, n_segments=0, p_none=0.4,
                                 rank_choices=(0, 0, 8, 16), d_in=512, d_out=768, page_elems=256)
-    say("[gpu] idle tokens pass through")
-    y, inst = _run(rt, wl, policy=1)
+    say(f"[gpu] idle tokens pass through policy={policy}")
+    y, inst = _run(rt, wl, policy=policy)
     ids = wl.token_adapter
     idle = (ids < 0) | (wl.ranks[np.maximum(ids, 0)] == 0)
     assert idle.any() and (~idle).any()
@@ -204,22 +225,23 @@ def test_fetch_byte_exact_and_sentinels(rt):
     inst.close()
 
 
-def test_probe_codes_bit_exact(rt):
-    """Integer-coded adapters: one-hot x reads back A^T codes exactly through shrink; one-hot
-    A^T rows route v = e_m to B row m exactly through apply (gathers and routing bit-exact)."""
+@pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
+def test_probe_codes_bit_exact(rt, policy):
+    """Integer-coded adapters: one-hot x reads back every A^T code exactly through shrink
+    (page gathers and token routing are bit-exact)."""
     for dt in ("f16", "bf16"):
         base_wl = workloads.random_small(204, dtype=dt, d_in=1536, d_out=1040, page_elems=512,
                                          n_tokens=24, n_segments=0, rank_choices=(4, 8, 16),
                                          p_none=0.0, n_adapters=5)
         wl = coded(base_wl)
-        say(f"[gpu] probe codes {dt}")
+        say(f"[gpu] probe codes {dt} policy={policy}")
         inst = rt.PagedLoRA(wl)
         p = wl.projections[0]
         js = np.random.default_rng(5).choice(p.d_in, size=wl.n_tokens)
         x = np.zeros((wl.n_tokens, p.d_in), np.float32)
         x[np.arange(wl.n_tokens), js] = 1.0
         xb = workloads.to_bits(x, dt)
-        call = inst.call(0, 1)
+        call = inst.call(0, policy)
         v = torch.zeros(wl.n_tokens, inst.r_max, dtype=torch.float32, device="cuda")
         ws = inst.workspace(call)
         inst.shrink(call, torch.from_numpy(xb.view(np.int16)).cuda(), v, ws)
@@ -268,17 +290,21 @@ def test_fetch_waits_and_free_state(rt):
     inst.close()
 
 
+LARGE = [("mixed_13b", 1), ("mlp_asym", 1), ("prefill_sgmv", 0), ("mixed_13b", 0),
+         ("mlp_asym", 2)]
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["mixed_13b", "mlp_asym"])
-def test_large_mbgmv_sampled(rt, name):
-    """Full-size workloads through MBGMV for every token, checked on sampled rows."""
+@pytest.mark.parametrize("name,policy", LARGE, ids=[f"{n}-{POLICY_IDS[p]}" for n, p in LARGE])
+def test_large_sampled(rt, name, policy):
+    """Full-size workloads, checked on sampled rows (segment ends, batch ends, random)."""
     wl = workloads.make(name)
-    say(f"[gpu] {name} (MBGMV for all tokens), building instance")
+    say(f"[gpu] {name} policy={policy}, building instance")
     inst = rt.PagedLoRA(wl)
     ev = sample_tokens(wl, 48)
     for proj in range(len(wl.projections)):
-        say(f"[gpu] {name} proj {wl.projections[proj].name}")
-        y, _ = _run(rt, wl, proj=proj, policy=1, inst=inst)
+        say(f"[gpu] {name} proj {wl.projections[proj].name} policy={policy}")
+        y, _ = _run(rt, wl, proj=proj, policy=policy, inst=inst)
         ref, _ = oracle_ref(wl, proj, ev)
         check_close(y[ev], ref, wl.dtype, f"{name}/{proj}")
         ids = np.concatenate([np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets)), wl.token_adapter])
