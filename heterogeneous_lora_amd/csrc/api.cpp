@@ -162,25 +162,27 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
   if (pv.n_sg) {
     // apply: k-range partials in the workspace; shrink / expand only: one range,
     // straight into / out of the caller's v
-    const int64_t stride = (int64_t)R->n_tokens * L->r_max;
+    int32_t v_stride = sg_v_stride(L->r_max);
     SgSplit sp = sg_split(L->d_in, pv.n_sg);
     float* vpart = (float*)(wsb + lay.sg_off);
     if (mode != kApply) {
       sp.ksplit = 1;
       sp.kc = (L->d_in + 127) / 128 * 128;
       vpart = mode == kShrink ? v_out : const_cast<float*>(v_in);
+      v_stride = L->r_max;
     }
+    const int64_t stride = (int64_t)R->n_tokens * v_stride;
     if (mode & kShrink) {
       e = timed_launch(SLORA_K_SGMV_SHRINK, s, [&] {
         return launch_sgmv_shrink(g, pv.tok, pv.sg, pv.n_sg, pv.sg_max_rank, sp.ksplit, sp.kc, x,
-                                  vpart, stride, s);
+                                  vpart, v_stride, stride, s);
       });
       if (e != hipSuccess) return hip_fail(e, "sgmv_shrink launch");
     }
     if (mode & kExpand) {
       e = timed_launch(SLORA_K_SGMV_EXPAND, s, [&] {
         return launch_sgmv_expand(g, pv.tok, pv.sg, pv.n_sg, pv.sg_max_rank, sp.ksplit, vpart,
-                                  stride, y, s);
+                                  v_stride, stride, y, s);
       });
       if (e != hipSuccess) return hip_fail(e, "sgmv_expand launch");
     }

@@ -32,6 +32,8 @@ inline int sg_max_split(int d_in) {
   const int s = d_in / 256;
   return s < 1 ? 1 : s > kSgMaxSplit ? kSgMaxSplit : s;
 }
+// Row stride of the SGMV partial v in the workspace (16-byte rows).
+inline int sg_v_stride(int r_max) { return (r_max + 3) / 4 * 4; }
 
 // Expand waves that split one column slice's rows: 1, 2 or 4 (4 waves per workgroup).
 inline int mb_split(int rank) { return rank <= 16 ? 1 : rank <= 32 ? 2 : 4; }
@@ -108,7 +110,7 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
 // Workspace (device, caller-owned, zero-filled once at allocation):
 //   [0, 256): header: uint64 tag of the last call whose wait gave up
 //   v_off: MBGMV v as uint64 words [n_tokens x r_max]: (tag << 32) | fp32 bits
-//   sg_off: SGMV partial v, fp32 [sg_max_split(d_in)][n_tokens x r_max]
+//   sg_off: SGMV partial v, fp32 [sg_max_split(d_in)][n_tokens x sg_v_stride(r_max)]
 constexpr int64_t kHeaderBytes = 256;
 struct WsLayout {
   int64_t v_off, sg_off, total;
@@ -124,19 +126,21 @@ hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, boo
                         uint32_t tag, unsigned long long* err, hipStream_t s);
 // Zero `bytes` (a multiple of 16) of device memory with a kernel.
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s);
-// SGMV shrink over ksplit k-ranges of kc (a multiple of 128) elements: range ks
-// writes its partial sums to vpart + ks * split_stride ([n_tokens x r_max] rows).
-// The expand adds the ksplit partials in range order.
+// SGMV shrink over ksplit (<= kSgMaxSplit) k-ranges of kc (a multiple of 128)
+// elements: range ks writes its partial sums to vpart + ks * split_stride, rows of
+// v_stride floats per token. The expand adds the ksplit partials in range order.
 struct SgSplit {
   int32_t ksplit, kc;
 };
 SgSplit sg_split(int32_t d_in, int32_t n_tiles);
 hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
-                              const void* x, float* vpart, int64_t split_stride, hipStream_t s);
+                              const void* x, float* vpart, int32_t v_stride, int64_t split_stride,
+                              hipStream_t s);
 hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, int32_t max_rank, int32_t ksplit,
-                              const float* vpart, int64_t split_stride, void* y, hipStream_t s);
+                              const float* vpart, int32_t v_stride, int64_t split_stride, void* y,
+                              hipStream_t s);
 
 constexpr int kFetchMaxPages = 240;
 struct FetchArgs {

@@ -296,7 +296,8 @@ WsLayout ws_layout(const slora_lora* L, const slora_routing* R) {
   const int64_t rows = T * std::max<int32_t>(L->r_max, 0);
   o.v_off = kHeaderBytes;
   o.sg_off = o.v_off + align_up(rows * 8, 256);
-  o.total = o.sg_off + align_up((int64_t)sg_max_split(std::max<int32_t>(L->d_in, 0)) * rows * 4, 256);
+  const int64_t sg_rows = T * sg_v_stride(std::max<int32_t>(L->r_max, 0));
+  o.total = o.sg_off + align_up((int64_t)sg_max_split(std::max<int32_t>(L->d_in, 0)) * sg_rows * 4, 256);
   return o;
 }
 

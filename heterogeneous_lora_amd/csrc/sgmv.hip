@@ -10,13 +10,13 @@
 // gets rows 4 * (l / 16) + q, q < 4, of column l % 16 of the fp32 result.
 //
 //   shrink (tile, k-range): v_part[ks][t][k] = sum over the k-range of x[t, j] A^T[k, j].
-//     Operands come straight from global memory with 16-byte loads: x rows (the
-//     tile's tokens) and A^T rows (rank rows, gathered through the page table)
-//     are both contiguous in j. The 4 waves take interleaved 32-wide steps of the
-//     k-range and add their partial products through LDS in a fixed order at the
-//     end. The k-ranges give the launch enough workgroups to fill the chip; the
-//     expand adds the ranges' partial sums in range order, so the result does not
-//     depend on scheduling.
+//     x rows (the tile's tokens) and A^T rows (rank rows, gathered through the
+//     page table) are both contiguous in j, so both operands are plain 16-byte
+//     loads. Each wave owns 16 tokens and reads its x rows straight from global
+//     memory; the A^T rows, which all 4 waves need, pass through LDS once per
+//     workgroup. The k-ranges give the launch enough workgroups to fill the chip;
+//     the expand adds the ranges' partial sums in range order, so the result does
+//     not depend on scheduling.
 //   expand (tile, 256 output columns): y[t, n] = RNE(y0 + s * sum_k v[t, k] B[k, n]).
 //     The product is computed transposed, D = B^T v^T, so that each lane ends up
 //     with 8 consecutive output columns of one token (16-byte y0 loads and y
@@ -59,110 +59,132 @@ __device__ __forceinline__ int tile_token(const SgTile& tl, const int32_t* tok, 
 }
 
 // ------------------------------------------------------------------ shrink
-// NB: 16-row blocks of rank rows (rank <= 16 * NB).
+// NB: 16-row blocks of rank rows (rank <= 16 * NB). Wave w owns the tile's token
+// rows 16 w .. 16 w + 15 and every rank row, so no partial sums cross waves.
+// The k-range is walked in batches of 128: the batch's A^T slab (16 NB rows x 256 B)
+// sits in one of two LDS buffers while the next batch's slab and x rows load into
+// registers. In the slab, the 16-byte segment s of row n is stored at position
+// s ^ (n % 16), so the 16 rows an MFMA operand read touches land in 16 different
+// bank groups.
+constexpr int kBatch = 4 * kStep;  // k per batch
+constexpr int kSegs = kBatch / 8;  // 16-byte segments per slab row
+
 template <int DT, int NB>
 __global__ __launch_bounds__(64 * kWaves) void sgmv_shrink_kernel(
     Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t kc,
-    const uint16_t* __restrict__ x, float* __restrict__ vpart, int64_t split_stride) {
-  extern __shared__ float red[];  // [3][4 * 4 * kRedCb][64] partial sums of waves 1..3
-  constexpr int kRedCb = NB < 4 ? NB : 4;
+    const uint16_t* __restrict__ x, float* __restrict__ vpart, int32_t v_stride,
+    int64_t split_stride) {
+  constexpr int kRows = 16 * NB;
+  constexpr int kLoads = kRows * kSegs / (64 * kWaves);  // slab vectors per thread
+  static_assert(kLoads >= 1 && kRows * kSegs == kLoads * 64 * kWaves, "slab split");
+  __shared__ uint4 slab[2][kRows * kSegs];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
   const SgTile tl = tiles[blockIdx.x];
   const int ks = blockIdx.y;
   const int kb = ks * kc, ke = min(g.d_in, kb + kc);
   const int r = tl.rank;
+  const int n_batch = (ke - kb + kBatch - 1) / kBatch;
 
-  int tk[4];  // this lane's operand rows: token of row tb * 16 + li
+  const int tk = tile_token(tl, tok, wave * 16 + li);  // this lane's x row
+  const uint16_t* xrow = tk >= 0 ? x + (int64_t)tk * g.d_in : nullptr;
+
+  // slab staging: thread -> slab position i * 256 + tid, i.e. row i * 16 + tid / 16 and
+  // stored segment tid % 16, which holds logical segment ls of that row
+  const int srow = tid >> 4, ls = (tid & 15) ^ srow;
+  const uint16_t* prow[kLoads];  // page of row i * 16 + srow in chunk cur_c, or a fill vector
+  bool preal[kLoads];
+  int cur_c = -1;
+  auto load_slab = [&](uint4 (&v)[kLoads], int bt) {
+    const int k = kb + bt * kBatch + ls * 8;
+    const bool live = k < ke;
+    const int c = live ? k / g.P : cur_c;
+    if (live && c != cur_c) {
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) tk[tb] = tile_token(tl, tok, tb * 16 + li);
+      for (int i = 0; i < kLoads; ++i) {
+        const int n = i * 16 + srow;
+        const uint16_t* p = fill_zero();
+        bool real = false;
+        if (n < r && c < g.cA) {
+          const int page = g.pt[(int64_t)tl.pt_base + (int64_t)n * g.cA + c];
+          real = (uint32_t)page < (uint64_t)g.n_pages;
+          p = real ? g.pool + (int64_t)page * g.P : fill_nan<DT>();
+        }
+        prow[i] = p;
+        preal[i] = real;
+      }
+      cur_c = c;
+    }
+    const int off = k - c * g.P;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      v[i] = ld16(!live ? fill_zero() : preal[i] ? prow[i] + off : prow[i]);
+  };
+  auto store_slab = [&](const uint4 (&v)[kLoads], int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) slab[buf][i * 256 + tid] = v[i];
+  };
+  auto load_x = [&](uint4 (&xv)[4], int bt) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = kb + bt * kBatch + s * kStep + kg * 8;
+      xv[s] = ld16(xrow && k < ke ? xrow + k : fill_zero());
+    }
+  };
 
-  // A^T row of each rank block for this lane, and the page it reads in chunk c
-  int k = kb + wave * kStep + kg * 8;  // this lane's first element
-  int c = k / g.P, off = k - c * g.P;
-  const uint16_t* arow[NB];  // page start, or a fill vector (then `areal` is false)
-  bool areal[NB];
-  auto load_pages = [&]() {
+  f32x4 acc[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const uint4 (&xv)[4], int buf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int n = cb * 16 + li;
+        const uint4 av = slab[buf][n * kSegs + ((s * 4 + kg) ^ li)];
+        acc[cb] = mfma<DT>(xv[s], av, acc[cb]);
+      }
+  };
+
+  // batch bt multiplies out of slab[bt % 2] and x buffer bt % 2 while batch bt + 1 loads
+  uint4 sv[kLoads], x0[4], x1[4];
+  if (n_batch > 0) {
+    load_slab(sv, 0);
+    load_x(x0, 0);
+    store_slab(sv, 0);
+    if (n_batch > 1) { load_slab(sv, 1); load_x(x1, 1); }
+  }
+  __syncthreads();
+  for (int bt = 0; bt < n_batch; bt += 2) {
+    mma(x0, 0);
+    if (bt + 1 >= n_batch) break;
+    store_slab(sv, 1);
+    if (bt + 2 < n_batch) { load_slab(sv, bt + 2); load_x(x0, bt + 2); }
+    __syncthreads();
+    mma(x1, 1);
+    if (bt + 2 >= n_batch) break;
+    store_slab(sv, 0);
+    if (bt + 3 < n_batch) { load_slab(sv, bt + 3); load_x(x1, bt + 3); }
+    __syncthreads();
+  }
+
+  // lane: token row 4 kg + q of this wave's block, rank row cb * 16 + li
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = __shfl(tk, 4 * kg + q);
+    if (t < 0) continue;
+    float* dst = vpart + ks * split_stride + (int64_t)t * v_stride;
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       const int n = cb * 16 + li;
-      const uint16_t* p = fill_zero();
-      bool real = false;
-      if (n < r && c < g.cA) {
-        const int page = g.pt[(int64_t)tl.pt_base + (int64_t)n * g.cA + c];
-        real = (uint32_t)page < (uint64_t)g.n_pages;
-        p = real ? g.pool + (int64_t)page * g.P : fill_nan<DT>();
-      }
-      arow[cb] = p;
-      areal[cb] = real;
+      if (n < r) dst[n] = acc[cb][q];
     }
-  };
-  load_pages();
-
-  f32x4 acc[4][NB];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) acc[tb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = kb + wave * kStep; k0 < ke; k0 += kRound) {
-    const bool live = k < ke;
-    uint4 xa[4], aa[NB];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      xa[tb] = ld16(live && tk[tb] >= 0 ? x + (int64_t)tk[tb] * g.d_in + k : fill_zero());
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
-      aa[cb] = ld16(!live ? fill_zero() : areal[cb] ? arow[cb] + off : arow[cb]);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) acc[tb][cb] = mfma<DT>(xa[tb], aa[cb], acc[tb][cb]);
-    k += kRound;
-    off += kRound;
-    if (off >= g.P) {  // crossed into the next chunk of every A^T row
-      while (off >= g.P) { off -= g.P; ++c; }
-      load_pages();
-    }
-  }
-
-  // waves 1..3 hand their partial sums to wave 0, which adds them in wave order
-#pragma unroll
-  for (int cb0 = 0; cb0 < NB; cb0 += kRedCb) {
-    if (wave > 0) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int cc = 0; cc < kRedCb; ++cc)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            red[(((wave - 1) * 4 + tb) * kRedCb * 4 + cc * 4 + q) * 64 + lane] = acc[tb][cb0 + cc][q];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-        for (int cc = 0; cc < kRedCb; ++cc) {
-          const int n = (cb0 + cc) * 16 + li;  // rank row of this lane's results
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float s = acc[tb][cb0 + cc][q];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-              s += red[(((w - 1) * 4 + tb) * kRedCb * 4 + cc * 4 + q) * 64 + lane];
-            const int t = __shfl(tk[tb], 4 * kg + q);  // token of result row 4 * kg + q
-            if (t >= 0 && n < r) vpart[ks * split_stride + (int64_t)t * g.r_max + n] = s;
-          }
-        }
-      }
-    }
-    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ expand
-constexpr int kCols = kSgCols;             // output columns per workgroup (64 per wave)
+constexpr int kCols = kSgCols;             // output columns of one pass (64 per wave)
+constexpr int kSubPasses = 4;              // passes per workgroup (1024 columns)
 constexpr int kBPitch = kCols + 4;         // B chunk row pitch in elements (bank spread)
 constexpr int kChunkRows = kStep;          // B rows staged per chunk
 
@@ -170,7 +192,8 @@ constexpr int kChunkRows = kStep;          // B rows staged per chunk
 template <int DT, int KB>
 __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
     Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t ksplit,
-    const float* __restrict__ vpart, int64_t split_stride, uint16_t* __restrict__ y) {
+    const float* __restrict__ vpart, int32_t v_stride, int64_t split_stride,
+    uint16_t* __restrict__ y) {
   constexpr int kRp = KB * kStep;     // padded rank
   constexpr int kVPitch = kRp + 8;    // v row pitch in elements
   __shared__ uint16_t vs[kTileRows * kVPitch];
@@ -178,68 +201,29 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
   const SgTile tl = tiles[blockIdx.x];
-  const int c0 = blockIdx.y * kCols;
   const int r = tl.rank;
+  const int col_begin = blockIdx.y * (kSubPasses * kCols);
+  const int n_pass = min(kSubPasses, (g.d_out - col_begin + kCols - 1) / kCols);
 
   int tk[4];  // token of operand row tb * 16 + li (the v^T operand's column)
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) tk[tb] = tile_token(tl, tok, tb * 16 + li);
 
-  // y0 of this lane's outputs: token tk[tb], columns c0 + wave * 64 + p * 32 + kg * 8 + [0, 8)
-  uint4 y0v[2][4];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int col = c0 + wave * 64 + p * 32 + kg * 8;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      y0v[p][tb] = ld16(tk[tb] >= 0 && col < g.d_out ? y + (int64_t)tk[tb] * g.d_out + col : fill_zero());
-  }
-
-  // v: sum of the k-range partials (in range order), rounded once, into LDS
-  {
-    constexpr int kThreadsPerRow = (64 * kWaves) / kTileRows;  // 4
-    constexpr int kPerThread = kRp / kThreadsPerRow;           // multiple of 4
-    static_assert(kPerThread % 4 == 0, "v staging split");
-    const int row = tid / kThreadsPerRow, part = tid % kThreadsPerRow;
-    const int t = tile_token(tl, tok, row);
-#pragma unroll
-    for (int q = 0; q < kPerThread; q += 4) {
-      const int kk = part * kPerThread + q;
-      float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t >= 0) {
-        for (int sp = 0; sp < ksplit; ++sp) {
-          const float* src = vpart + sp * split_stride + (int64_t)t * g.r_max + kk;
-          // rows at or past the rank were never written: read as zero
-          float4 a;
-          a.x = kk + 0 < r ? src[0] : 0.f;
-          a.y = kk + 1 < r ? src[1] : 0.f;
-          a.z = kk + 2 < r ? src[2] : 0.f;
-          a.w = kk + 3 < r ? src[3] : 0.f;
-          s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
-        }
-      }
-      uint2 packed;
-      packed.x = pack2<DT>(s.x, s.y);
-      packed.y = pack2<DT>(s.z, s.w);
-      *reinterpret_cast<uint2*>(&vs[row * kVPitch + kk]) = packed;
-    }
-  }
-
-  // B staging: thread -> column slot (8 columns) and rows; its page chunk is fixed
-  const int slot = tid & 31, row0 = tid >> 5;  // 8 rows per pass, 4 passes per chunk
-  const int bcol = c0 + slot * 8;
-  const bool bcol_live = bcol < g.d_out;
-  const int bc = bcol_live ? bcol / g.P : 0;
-  const int boff = bcol - bc * g.P;
-  const int64_t bbase = (int64_t)tl.pt_base + (int64_t)r * g.cA + bc;
-  auto load_b = [&](uint4 (&b)[4], int chunk) {
+  // B staging: thread -> column slot (8 columns) and rows row0 + 8 i of a chunk
+  const int slot = tid & 31, row0 = tid >> 5;
+  auto load_b = [&](uint4 (&b)[4], int j) {  // chunk j % KB of pass j / KB
+    const int bcol = col_begin + (j / KB) * kCols + slot * 8;
+    const bool live = bcol < g.d_out;
+    const int bc = live ? bcol / g.P : 0;
+    const int64_t bbase = (int64_t)tl.pt_base + (int64_t)r * g.cA + bc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kr = chunk * kChunkRows + row0 + i * 8;
+      const int kr = (j % KB) * kChunkRows + row0 + i * 8;
       const uint16_t* p = fill_zero();
-      if (bcol_live && kr < r) {
+      if (live && kr < r) {
         const int page = g.pt[bbase + (int64_t)kr * g.cB];
-        p = (uint32_t)page < (uint64_t)g.n_pages ? g.pool + (int64_t)page * g.P + boff : fill_nan<DT>();
+        p = (uint32_t)page < (uint64_t)g.n_pages ? g.pool + (int64_t)page * g.P + (bcol - bc * g.P)
+                                                 : fill_nan<DT>();
       }
       b[i] = ld16(p);
     }
@@ -252,22 +236,77 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
       d[1] = make_uint2(b[i].z, b[i].w);
     }
   };
-
-  f32x4 acc[2][2][4];  // [pair][half][token block]
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[p][h][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   uint4 bn[4];
-  load_b(bn, 0);
+  load_b(bn, 0);  // in flight while v is staged
+
+  // v: the k-range partials added in range order, rounded once, into LDS. Thread:
+  // row tid / 4, columns 16 q + 4 (tid % 4) + [0, 4); rows at or past the rank
+  // were never written and read as zero.
+  {
+    const int row = tid >> 2, cq = (tid & 3) * 4;
+    const int t = tile_token(tl, tok, row);
+    const bool vec = (v_stride & 3) == 0;
 #pragma unroll
-  for (int ch = 0; ch < KB; ++ch) {
-    if (ch > 0) __syncthreads();  // the previous chunk has been read
+    for (int q = 0; q < kRp / 16; ++q) {
+      const int kk = q * 16 + cq;
+      float4 a[kSgMaxSplit];
+#pragma unroll
+      for (int sp = 0; sp < kSgMaxSplit; ++sp) {
+        a[sp] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (sp < ksplit && t >= 0 && kk < r) {
+          const float* src = vpart + sp * split_stride + (int64_t)t * v_stride + kk;
+          if (vec) {
+            a[sp] = *reinterpret_cast<const float4*>(src);
+          } else {
+            a[sp].x = src[0];
+            a[sp].y = kk + 1 < r ? src[1] : 0.f;
+            a[sp].z = kk + 2 < r ? src[2] : 0.f;
+            a[sp].w = kk + 3 < r ? src[3] : 0.f;
+          }
+        }
+      }
+      float4 sum = a[0];
+#pragma unroll
+      for (int sp = 1; sp < kSgMaxSplit; ++sp) {
+        sum.x += a[sp].x; sum.y += a[sp].y; sum.z += a[sp].z; sum.w += a[sp].w;
+      }
+      sum.y = kk + 1 < r ? sum.y : 0.f;
+      sum.z = kk + 2 < r ? sum.z : 0.f;
+      sum.w = kk + 3 < r ? sum.w : 0.f;
+      uint2 packed;
+      packed.x = pack2<DT>(sum.x, sum.y);
+      packed.y = pack2<DT>(sum.z, sum.w);
+      *reinterpret_cast<uint2*>(&vs[row * kVPitch + kk]) = packed;
+    }
+  }
+
+  const float s = tl.scale;
+  f32x4 acc[2][2][4];  // [pair][half][token block]
+  uint4 y0v[2][4];
+  const int n_j = n_pass * KB;
+  for (int j = 0; j < n_j; ++j) {
+    const int pass = j / KB, ch = j % KB;
+    const int cw = col_begin + pass * kCols + wave * 64;  // this wave's first column
+    if (ch == 0) {
+      // y0 of this lane's outputs: token tk[tb], columns cw + p * 32 + kg * 8 + [0, 8)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int col = cw + p * 32 + kg * 8;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          y0v[p][tb] = ld16(tk[tb] >= 0 && col < g.d_out ? y + (int64_t)tk[tb] * g.d_out + col
+                                                         : fill_zero());
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) acc[p][h][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();  // v is staged / the previous chunk has been read
     store_b(bn);
-    if (ch + 1 < KB) load_b(bn, ch + 1);
+    if (j + 1 < n_j) load_b(bn, j + 1);
     __syncthreads();
     // v^T operand: token tb * 16 + li, k = ch * 32 + kg * 8 + [0, 8)
     uint4 vo[4];
@@ -290,24 +329,24 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[p][h][tb] = mfma<DT>(bo, vo[tb], acc[p][h][tb]);
       }
-  }
-
-  // lane: token tk[tb], columns c0 + wave * 64 + p * 32 + kg * 8 + h * 4 + q
-  const float s = tl.scale;
+    if (ch == KB - 1) {
+      // lane: token tk[tb], columns cw + p * 32 + kg * 8 + h * 4 + q
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int col = c0 + wave * 64 + p * 32 + kg * 8;
+      for (int p = 0; p < 2; ++p) {
+        const int col = cw + p * 32 + kg * 8;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      if (tk[tb] < 0 || col >= g.d_out) continue;
-      const uint4 y0 = y0v[p][tb];
-      const f32x4 a = acc[p][0][tb], b = acc[p][1][tb];
-      uint4 o;
-      o.x = pack2<DT>(fmaf(s, a[0], lo_f32<DT>(y0.x)), fmaf(s, a[1], hi_f32<DT>(y0.x)));
-      o.y = pack2<DT>(fmaf(s, a[2], lo_f32<DT>(y0.y)), fmaf(s, a[3], hi_f32<DT>(y0.y)));
-      o.z = pack2<DT>(fmaf(s, b[0], lo_f32<DT>(y0.z)), fmaf(s, b[1], hi_f32<DT>(y0.z)));
-      o.w = pack2<DT>(fmaf(s, b[2], lo_f32<DT>(y0.w)), fmaf(s, b[3], hi_f32<DT>(y0.w)));
-      st16(y + (int64_t)tk[tb] * g.d_out + col, o);
+        for (int tb = 0; tb < 4; ++tb) {
+          if (tk[tb] < 0 || col >= g.d_out) continue;
+          const uint4 y0 = y0v[p][tb];
+          const f32x4 a = acc[p][0][tb], b = acc[p][1][tb];
+          uint4 o;
+          o.x = pack2<DT>(fmaf(s, a[0], lo_f32<DT>(y0.x)), fmaf(s, a[1], hi_f32<DT>(y0.x)));
+          o.y = pack2<DT>(fmaf(s, a[2], lo_f32<DT>(y0.y)), fmaf(s, a[3], hi_f32<DT>(y0.y)));
+          o.z = pack2<DT>(fmaf(s, b[0], lo_f32<DT>(y0.z)), fmaf(s, b[1], hi_f32<DT>(y0.z)));
+          o.w = pack2<DT>(fmaf(s, b[2], lo_f32<DT>(y0.w)), fmaf(s, b[3], hi_f32<DT>(y0.w)));
+          st16(y + (int64_t)tk[tb] * g.d_out + col, o);
+        }
+      }
     }
   }
 }
@@ -315,29 +354,30 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
 template <int DT>
 hipError_t shrink_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
                      int32_t ksplit, int32_t kc, int32_t nb, const void* x, float* vpart,
-                     int64_t split_stride, hipStream_t s) {
+                     int32_t v_stride, int64_t split_stride, hipStream_t s) {
   const dim3 grid((unsigned)n_tiles, (unsigned)ksplit), block(64 * kWaves);
-  const size_t lds = (size_t)3 * 4 * (nb < 4 ? nb : 4) * 4 * 64 * sizeof(float);
+  const size_t lds = 0;
   const uint16_t* xp = (const uint16_t*)x;
   switch (nb) {
-    case 1: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 1>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, split_stride); break;
-    case 2: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 2>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, split_stride); break;
-    case 4: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 4>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, split_stride); break;
-    default: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 8>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, split_stride); break;
+    case 1: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 1>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
+    case 2: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 2>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
+    case 4: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 4>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
+    default: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 8>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
   }
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t expand_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
-                     int32_t ksplit, int32_t kb, const float* vpart, int64_t split_stride, void* y,
-                     hipStream_t s) {
-  const dim3 grid((unsigned)n_tiles, (unsigned)((g.d_out + kCols - 1) / kCols)), block(64 * kWaves);
+                     int32_t ksplit, int32_t kb, const float* vpart, int32_t v_stride,
+                     int64_t split_stride, void* y, hipStream_t s) {
+  const int per_wg = kSubPasses * kCols;
+  const dim3 grid((unsigned)n_tiles, (unsigned)((g.d_out + per_wg - 1) / per_wg)), block(64 * kWaves);
   uint16_t* yp = (uint16_t*)y;
   switch (kb) {
-    case 1: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 1>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, split_stride, yp); break;
-    case 2: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 2>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, split_stride, yp); break;
-    default: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 4>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, split_stride, yp); break;
+    case 1: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 1>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
+    case 2: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 2>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
+    default: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 4>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
   }
   return hipGetLastError();
 }
@@ -356,24 +396,28 @@ SgSplit sg_split(int32_t d_in, int32_t n_tiles) {
 
 hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
-                              const void* x, float* vpart, int64_t split_stride, hipStream_t s) {
+                              const void* x, float* vpart, int32_t v_stride, int64_t split_stride,
+                              hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || kc % kRound) return hipErrorInvalidValue;
+  if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit || kc % kRound)
+    return hipErrorInvalidValue;
   const int nb = max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8;
   return g.dtype == SLORA_F16
-             ? shrink_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, split_stride, s)
-             : shrink_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, split_stride, s);
+             ? shrink_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, v_stride, split_stride, s)
+             : shrink_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, v_stride, split_stride, s);
 }
 
 hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, int32_t max_rank, int32_t ksplit,
-                              const float* vpart, int64_t split_stride, void* y, hipStream_t s) {
+                              const float* vpart, int32_t v_stride, int64_t split_stride, void* y,
+                              hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1) return hipErrorInvalidValue;
+  if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit)
+    return hipErrorInvalidValue;
   const int kb = max_rank <= 32 ? 1 : max_rank <= 64 ? 2 : 4;
   return g.dtype == SLORA_F16
-             ? expand_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kb, vpart, split_stride, y, s)
-             : expand_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kb, vpart, split_stride, y, s);
+             ? expand_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kb, vpart, v_stride, split_stride, y, s)
+             : expand_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kb, vpart, v_stride, split_stride, y, s);
 }
 
 }  // namespace slora
