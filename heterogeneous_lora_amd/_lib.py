@@ -53,6 +53,13 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with heterogeneous_lora_amd/build.py")
+    # The library and torch must share one HIP runtime. torch ships its own copy of
+    # libamdhip64; loading torch first makes the library bind to that copy (same soname)
+    # instead of pulling a second runtime into the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I = _vp, _c_i32
     sig = {

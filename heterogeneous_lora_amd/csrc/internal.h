@@ -24,7 +24,6 @@ constexpr int kMbExpandTok = 2;     // MBGMV expand: tokens per workgroup
 constexpr int kMbWaveCols = 512;    // MBGMV expand: output columns per wave (64 lanes x 8)
 constexpr int kMbRowsPerWave = 16;  // MBGMV expand: B rows a wave keeps in flight
 constexpr int kSgTile = 64;         // SGMV: tokens per tile
-constexpr int kSgCols = 256;        // SGMV expand: output columns per workgroup
 constexpr int kSgMaxSplit = 8;      // SGMV shrink: most k-ranges d_in is cut into
 
 // k-ranges the SGMV shrink may cut d_in into (each at least 256 long).

@@ -17,12 +17,13 @@
 //     workgroup. The k-ranges give the launch enough workgroups to fill the chip;
 //     the expand adds the ranges' partial sums in range order, so the result does
 //     not depend on scheduling.
-//   expand (tile, 256 output columns): y[t, n] = RNE(y0 + s * sum_k v[t, k] B[k, n]).
+//   expand (tile, 1024 output columns): y[t, n] = RNE(y0 + s * sum_k v[t, k] B[k, n]).
 //     The product is computed transposed, D = B^T v^T, so that each lane ends up
 //     with 8 consecutive output columns of one token (16-byte y0 loads and y
 //     stores). v (summed over k-ranges, rounded once to the storage type to feed
-//     the matrix cores) and 32-row chunks of B are staged in LDS; the B^T operand
-//     is read out of LDS column-wise.
+//     the matrix cores) is staged in LDS once; the columns are walked in passes of
+//     128 (32 per wave) whose B rows pass through LDS in 32-row chunks, the B^T
+//     operand read out column-wise, while the next pass's y0 is already loading.
 #include <algorithm>
 
 #include "device_common.h"
@@ -183,8 +184,8 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_shrink_kernel(
 }
 
 // ------------------------------------------------------------------ expand
-constexpr int kCols = kSgCols;             // output columns of one pass (64 per wave)
-constexpr int kSubPasses = 4;              // passes per workgroup (1024 columns)
+constexpr int kCols = 128;                 // output columns of one pass (32 per wave)
+constexpr int kSubPasses = 8;              // passes per workgroup (1024 columns)
 constexpr int kBPitch = kCols + 4;         // B chunk row pitch in elements (bank spread)
 constexpr int kChunkRows = kStep;          // B rows staged per chunk
 
@@ -209,16 +210,17 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) tk[tb] = tile_token(tl, tok, tb * 16 + li);
 
-  // B staging: thread -> column slot (8 columns) and rows row0 + 8 i of a chunk
-  const int slot = tid & 31, row0 = tid >> 5;
-  auto load_b = [&](uint4 (&b)[4], int j) {  // chunk j % KB of pass j / KB
+  // B staging: thread -> column slot (8 columns) and rows row0 + 16 i of a chunk
+  constexpr int kSlots = kCols / 8, kRowStep = 64 * kWaves / kSlots, kBLoads = kChunkRows / kRowStep;
+  const int slot = tid % kSlots, row0 = tid / kSlots;
+  auto load_b = [&](uint4 (&b)[kBLoads], int j) {  // chunk j % KB of pass j / KB
     const int bcol = col_begin + (j / KB) * kCols + slot * 8;
     const bool live = bcol < g.d_out;
     const int bc = live ? bcol / g.P : 0;
     const int64_t bbase = (int64_t)tl.pt_base + (int64_t)r * g.cA + bc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = (j % KB) * kChunkRows + row0 + i * 8;
+    for (int i = 0; i < kBLoads; ++i) {
+      const int kr = (j % KB) * kChunkRows + row0 + i * kRowStep;
       const uint16_t* p = fill_zero();
       if (live && kr < r) {
         const int page = g.pt[bbase + (int64_t)kr * g.cB];
@@ -228,15 +230,15 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
       b[i] = ld16(p);
     }
   };
-  auto store_b = [&](const uint4 (&b)[4]) {
+  auto store_b = [&](const uint4 (&b)[kBLoads]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint2* d = reinterpret_cast<uint2*>(&bs[(row0 + i * 8) * kBPitch + slot * 8]);
+    for (int i = 0; i < kBLoads; ++i) {
+      uint2* d = reinterpret_cast<uint2*>(&bs[(row0 + i * kRowStep) * kBPitch + slot * 8]);
       d[0] = make_uint2(b[i].x, b[i].y);
       d[1] = make_uint2(b[i].z, b[i].w);
     }
   };
-  uint4 bn[4];
+  uint4 bn[kBLoads];
   load_b(bn, 0);  // in flight while v is staged
 
   // v: the k-range partials added in range order, rounded once, into LDS. Thread:
@@ -281,45 +283,37 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
   }
 
   const float s = tl.scale;
-  f32x4 acc[2][2][4];  // [pair][half][token block]
-  uint4 y0v[2][4];
   const int n_j = n_pass * KB;
-  for (int j = 0; j < n_j; ++j) {
-    const int pass = j / KB, ch = j % KB;
-    const int cw = col_begin + pass * kCols + wave * 64;  // this wave's first column
-    if (ch == 0) {
-      // y0 of this lane's outputs: token tk[tb], columns cw + p * 32 + kg * 8 + [0, 8)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int col = cw + p * 32 + kg * 8;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-          y0v[p][tb] = ld16(tk[tb] >= 0 && col < g.d_out ? y + (int64_t)tk[tb] * g.d_out + col
-                                                         : fill_zero());
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) acc[p][h][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    __syncthreads();  // v is staged / the previous chunk has been read
-    store_b(bn);
-    if (j + 1 < n_j) load_b(bn, j + 1);
-    __syncthreads();
-    // v^T operand: token tb * 16 + li, k = ch * 32 + kg * 8 + [0, 8)
-    uint4 vo[4];
+  // y0 of this lane's outputs in a pass: token tk[tb], columns cw + kg * 8 + [0, 8)
+  auto load_y0 = [&](uint4 (&yv)[4], int pass) {
+    const int col = col_begin + pass * kCols + wave * 32 + kg * 8;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
-      vo[tb] = *reinterpret_cast<const uint4*>(&vs[(tb * 16 + li) * kVPitch + ch * kStep + kg * 8]);
-    // B^T operand: output column (p, h, li) = p * 32 + (li / 4) * 8 + h * 4 + li % 4 of this
-    // wave's 64, k = kg * 8 + [0, 8) of the chunk
+      yv[tb] = ld16(tk[tb] >= 0 && col < g.d_out ? y + (int64_t)tk[tb] * g.d_out + col : fill_zero());
+  };
+  auto run_pass = [&](int pass, const uint4 (&yv)[4]) {
+    f32x4 acc[2][4];  // [half][token block]
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[h][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < KB; ++ch) {
+      const int j = pass * KB + ch;
+      __syncthreads();  // v is staged / the previous chunk has been read
+      store_b(bn);
+      if (j + 1 < n_j) load_b(bn, j + 1);
+      __syncthreads();
+      // v^T operand: token tb * 16 + li, k = ch * 32 + kg * 8 + [0, 8)
+      uint4 vo[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        vo[tb] = *reinterpret_cast<const uint4*>(&vs[(tb * 16 + li) * kVPitch + ch * kStep + kg * 8]);
+      // B^T operand: output column (h, li) = (li / 4) * 8 + h * 4 + li % 4 of this wave's 32,
+      // k = kg * 8 + [0, 8) of the chunk
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int colw = wave * 64 + p * 32 + (li >> 2) * 8 + h * 4 + (li & 3);
+        const int colw = wave * 32 + (li >> 2) * 8 + h * 4 + (li & 3);
         const uint16_t* src = &bs[(kg * 8) * kBPitch + colw];
         uint4 bo;
         bo.x = (uint32_t)src[0 * kBPitch] | ((uint32_t)src[1 * kBPitch] << 16);
@@ -327,27 +321,34 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
         bo.z = (uint32_t)src[4 * kBPitch] | ((uint32_t)src[5 * kBPitch] << 16);
         bo.w = (uint32_t)src[6 * kBPitch] | ((uint32_t)src[7 * kBPitch] << 16);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[p][h][tb] = mfma<DT>(bo, vo[tb], acc[p][h][tb]);
-      }
-    if (ch == KB - 1) {
-      // lane: token tk[tb], columns cw + p * 32 + kg * 8 + h * 4 + q
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int col = cw + p * 32 + kg * 8;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          if (tk[tb] < 0 || col >= g.d_out) continue;
-          const uint4 y0 = y0v[p][tb];
-          const f32x4 a = acc[p][0][tb], b = acc[p][1][tb];
-          uint4 o;
-          o.x = pack2<DT>(fmaf(s, a[0], lo_f32<DT>(y0.x)), fmaf(s, a[1], hi_f32<DT>(y0.x)));
-          o.y = pack2<DT>(fmaf(s, a[2], lo_f32<DT>(y0.y)), fmaf(s, a[3], hi_f32<DT>(y0.y)));
-          o.z = pack2<DT>(fmaf(s, b[0], lo_f32<DT>(y0.z)), fmaf(s, b[1], hi_f32<DT>(y0.z)));
-          o.w = pack2<DT>(fmaf(s, b[2], lo_f32<DT>(y0.w)), fmaf(s, b[3], hi_f32<DT>(y0.w)));
-          st16(y + (int64_t)tk[tb] * g.d_out + col, o);
-        }
+        for (int tb = 0; tb < 4; ++tb) acc[h][tb] = mfma<DT>(bo, vo[tb], acc[h][tb]);
       }
     }
+    // lane: token tk[tb], columns col + h * 4 + q
+    const int col = col_begin + pass * kCols + wave * 32 + kg * 8;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      if (tk[tb] < 0 || col >= g.d_out) continue;
+      const uint4 y0 = yv[tb];
+      const f32x4 a = acc[0][tb], b = acc[1][tb];
+      uint4 o;
+      o.x = pack2<DT>(fmaf(s, a[0], lo_f32<DT>(y0.x)), fmaf(s, a[1], hi_f32<DT>(y0.x)));
+      o.y = pack2<DT>(fmaf(s, a[2], lo_f32<DT>(y0.y)), fmaf(s, a[3], hi_f32<DT>(y0.y)));
+      o.z = pack2<DT>(fmaf(s, b[0], lo_f32<DT>(y0.z)), fmaf(s, b[1], hi_f32<DT>(y0.z)));
+      o.w = pack2<DT>(fmaf(s, b[2], lo_f32<DT>(y0.w)), fmaf(s, b[3], hi_f32<DT>(y0.w)));
+      st16(y + (int64_t)tk[tb] * g.d_out + col, o);
+    }
+  };
+
+  // y0 of the next pass loads while a pass multiplies (two named buffers)
+  uint4 ya[4], yb[4];
+  load_y0(ya, 0);
+  for (int pass = 0; pass < n_pass; pass += 2) {
+    if (pass + 1 < n_pass) load_y0(yb, pass + 1);
+    run_pass(pass, ya);
+    if (pass + 1 >= n_pass) break;
+    if (pass + 2 < n_pass) load_y0(ya, pass + 2);
+    run_pass(pass + 1, yb);
   }
 }
 
