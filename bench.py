@@ -72,21 +72,81 @@ def algorithmic(wl, proj, policy):
     return out
 
 
+# Source files each kernel family is compiled from (a counter summary is void once they change).
+KERNEL_SOURCES = {
+    fam: [f"heterogeneous_lora_amd/csrc/{fam}.hip", "heterogeneous_lora_amd/csrc/device_common.h",
+          "heterogeneous_lora_amd/csrc/internal.h"]
+    for fam in ("mbgmv", "sgmv")
+}
+
+
+def sources_sha256(kernel):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel.split("_")[0]]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def load_traffic(kernel, workload):
     """HBM traffic per launch from a committed rocprofv3 PMC summary, or None when the
-    summary is missing or the kernel source changed since the counters were taken."""
+    summary is missing or the kernel's sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    src = os.path.join(ROOT, d["source"])
-    if not os.path.exists(src):
-        return None
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if h != d.get("source_sha256"):
+    if d.get("sources_sha256") != sources_sha256(kernel):
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def calib_copy(nbytes, reps):
+    """A plain device-to-device copy of known size (the reference the byte counters are
+    scaled by): `reps` launches of torch's copy kernel over nbytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": nbytes, "launches": reps}), flush=True)
+
+
+def _pmc_mean_kib(path, match, counter):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if match in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {match!r} in {path}")
+    return float(np.mean(vals)), len(vals)
+
+
+def pmc_summary(a):
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of a kernel and of the
+    calibration copy into HBM bytes per launch; writes profiles/pmc_<kernel>_<workload>.json."""
+    fk, fn = _pmc_mean_kib(a.fetch_csv, a.match, "FETCH_SIZE")
+    wk, wn = _pmc_mean_kib(a.write_csv, a.match, "WRITE_SIZE")
+    cfk, _ = _pmc_mean_kib(a.calib_fetch_csv, a.calib_match, "FETCH_SIZE")
+    cwk, _ = _pmc_mean_kib(a.calib_write_csv, a.calib_match, "WRITE_SIZE")
+    f_scale = a.calib_bytes / (cfk * 1024.0)
+    w_scale = a.calib_bytes / (cwk * 1024.0)
+    out = {
+        "kernel": a.kernel, "workload": a.workload,
+        "sources": KERNEL_SOURCES[a.kernel.split("_")[0]], "sources_sha256": sources_sha256(a.kernel),
+        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+        "dispatches": [fn, wn],
+        "calib_copy_bytes": a.calib_bytes,
+        "calib_fetch_kib": round(cfk, 1), "calib_write_kib": round(cwk, 1),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "traffic_bytes_per_launch": int(fk * 1024 * f_scale + wk * 1024 * w_scale),
+        "commands": a.commands.split(" ;; ") if a.commands else [],
+    }
+    path = os.path.join(ROOT, "profiles", f"pmc_{a.kernel}_{a.workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(wl, budget_s):
@@ -138,11 +198,28 @@ def main():
     ap.add_argument("--instances", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="time the kernels of one step in this many with HIP events")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
+                    help="only run the plain copy the byte counters are calibrated with")
+    ap.add_argument("--pmc-summary", action="store_true",
+                    help="only summarize rocprofv3 FETCH_SIZE / WRITE_SIZE runs (no GPU)")
+    for opt in ("kernel", "workload", "match", "fetch-csv", "write-csv", "calib-match",
+                "calib-fetch-csv", "calib-write-csv", "commands"):
+        ap.add_argument(f"--{opt}", default="")
+    ap.add_argument("--calib-bytes", type=int, default=0)
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would own "
-              "its pool and serve its own requests); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: each GPU would own its pool and serve its own "
+              "requests, with no exchange between GPUs on this path; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
+    if args.calib_copy:
+        calib_copy(args.calib_copy, 20)
+        return
 
     import torch
     import workloads
@@ -173,19 +250,29 @@ def main():
                       for p in wl.projections)
 
     stream = torch.cuda.current_stream(dev)
+    # per instance and projection, the apply call with its arguments marshalled once
+    bound = [[inst.bind_apply(calls[p], io[p][0], io[p][1], ws, stream) for p in range(n_proj)]
+             for inst, calls, io, ws in insts]
 
     def step(i):
-        inst, calls, io, ws = insts[i % len(insts)]
-        for p in range(n_proj):
-            inst.apply(calls[p], io[p][0], io[p][1], ws, stream)
+        for run in bound[i % len(bound)]:
+            run()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    _lib.timing_enable(True)
+    _lib.timing_read()  # start from empty kernel counters
+    # HIP events bracket every kernel of one step in `event_every` (recording them costs
+    # the host a few microseconds per launch, which would otherwise pace the loop)
+    ev = max(1, args.event_every)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        if i % ev == 0:
+            _lib.timing_enable(True)
+            step(i)
+            _lib.timing_enable(False)
+        else:
+            step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     timing = _lib.timing_read()
@@ -217,8 +304,9 @@ def main():
                 "unit": "GB/s", "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic}
     if sgmv_like:
         roofline["mfma_frac"] = round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
-    kern_total_s = sum(ms for n, ms in timing.values()) * 1e-3 / args.steps
-    step_bytes = sum(kv["algorithmic_bytes"] * kv["launches"] for kv in kernels.values()) / args.steps
+    n_timed = (args.steps + ev - 1) // ev
+    kern_total_s = sum(ms for n, ms in timing.values()) * 1e-3 / n_timed
+    step_bytes = sum(kv["algorithmic_bytes"] * kv["launches"] for kv in kernels.values()) / n_timed
     log(f"[bench] kernels: {json.dumps(kernels)}")
     log(f"[bench] all kernels of a step: {kern_total_s * 1e6:.1f} us, "
         f"{step_bytes / kern_total_s / 1e9:.0f} GB/s algorithmic")
@@ -242,6 +330,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "kernel_timing": f"HIP events on the launch stream around every kernel of 1 step in {ev}",
         "step_kernel_us": round(kern_total_s * 1e6, 2),
         "step_algorithmic_gbps": round(step_bytes / kern_total_s / 1e9, 1),
         "fetch": {"bytes": fetch_bytes, "ms": round(float(np.median(fetch_ms)), 3),

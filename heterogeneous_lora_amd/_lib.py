@@ -224,6 +224,22 @@ def apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
                               _vp(ws), ws_bytes, _vp(stream)), "apply")
 
 
+def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
+    """slora_apply with its arguments converted once: returns a no-argument callable for
+    callers that repeat the same call (same buffers, new contents) many times."""
+    f = load().slora_apply
+    args = (ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(x), _vp(y), _vp(ws),
+            _c_i64(ws_bytes), _vp(stream))
+
+    def run():
+        rc = f(*args)
+        if rc != OK:
+            _check(rc, "apply")
+
+    run.call = call  # the argument structs must outlive the callable
+    return run
+
+
 KERNELS = ["mbgmv_shrink", "mbgmv_expand", "sgmv_shrink", "sgmv_expand", "mbgmv_fused"]
 
 

@@ -221,8 +221,6 @@ int slora_timing_enable(int32_t on) {
   clear_error();
   std::lock_guard<std::mutex> lk(g_mu);
   g_timing_on = on != 0;
-  for (auto& t : g_timed) g_spare_events.push_back({t.start, t.stop});
-  g_timed.clear();
   return SLORA_OK;
 }
 
@@ -304,12 +302,12 @@ int slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int
     if (it.part != 0) continue;
     info[5 * at + 0] = 0;
     info[5 * at + 1] = slot;
-    info[5 * at + 2] = it.n_tok;
+    info[5 * at + 2] = it.n_tok();
     info[5 * at + 3] = it.pt_base;
     info[5 * at + 4] = it.rank;
     if (tokens)
-      for (int32_t t = 0; t < it.n_tok; ++t) tokens[slot + t] = it.tok[t];
-    slot += it.n_tok;
+      for (int32_t t = 0; t < it.n_tok(); ++t) tokens[slot + t] = it.tok[t];
+    slot += it.n_tok();
     ++at;
   }
   for (int32_t i = 0; i < pv.n_sg; ++i) {
@@ -320,7 +318,8 @@ int slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int
     info[5 * at + 3] = t.pt_base;
     info[5 * at + 4] = t.rank;
     if (tokens)
-      for (int32_t q = 0; q < t.n_tok; ++q) tokens[slot + q] = pv.tok[t.tok_begin + q];
+      for (int32_t q = 0; q < t.n_tok; ++q)
+        tokens[slot + q] = t.first_tok >= 0 ? t.first_tok + q : pv.tok[t.tok_begin + q];
     slot += t.n_tok;
     ++at;
   }

@@ -37,21 +37,26 @@ inline int sg_v_stride(int r_max) { return (r_max + 3) / 4 * 4; }
 // Expand waves that split one column slice's rows: 1, 2 or 4 (4 waves per workgroup).
 inline int mb_split(int rank) { return rank <= 16 ? 1 : rank <= 32 ? 2 : 4; }
 
-// One MBGMV work item (one workgroup), 64 bytes, read by the kernel straight from
+// One MBGMV work item (one workgroup), 32 bytes, read by the kernel straight from
 // the pinned staging buffer. Token ids are inline so a workgroup needs one load to
 // know all it has to read.
 struct MbItem {
-  int32_t tok[kMbGroup];  // token ids (n_tok of them)
-  int32_t n_tok;
+  int32_t tok[kMbGroup];  // token ids (n_tok() of them)
   int32_t pt_base;        // page-table entry of the adapter's A^T row 0, chunk 0
-  int32_t rank;
   float scale;
-  int32_t role;           // 0 = shrink, 1 = expand
-  int32_t part;           // shrink: row block; expand: column tile
-  int32_t split;          // expand: waves sharing a column slice (mb_split(rank))
-  int32_t pad[5];
+  int16_t part;           // shrink: row block; expand: column tile
+  uint8_t rank;           // 1 .. kMaxRank
+  uint8_t info;           // bits 0-2: n_tok; bit 3: role (0 shrink, 1 expand); bits 4-6: split
+  int32_t pad;
+  __host__ __device__ int n_tok() const { return info & 7; }
+  __host__ __device__ int role() const { return (info >> 3) & 1; }
+  __host__ __device__ int split() const { return (info >> 4) & 7; }  // expand: mb_split(rank)
+  __host__ __device__ static uint8_t pack_info(int n_tok, int role, int split) {
+    return (uint8_t)(n_tok | (role << 3) | (split << 4));
+  }
 };
-static_assert(sizeof(MbItem) == 64, "MbItem layout");
+static_assert(sizeof(MbItem) == 32, "MbItem layout");
+static_assert(kMaxRank <= 255, "rank is stored in 8 bits");
 
 // One SGMV tile: up to kSgTile tokens of one adapter. 32 bytes.
 struct SgTile {
@@ -93,10 +98,13 @@ struct PlanView {
 
 // Scratch the planner reuses between calls (thread-local, grows only).
 struct PlanScratch {
-  std::vector<uint64_t> mb_keys, sg_keys;    // (adapter << 32 | token), sorted
-  std::vector<int32_t> grp;                  // MBGMV groups: (key index, count, adapter) triples
-  std::vector<int32_t> tiles;                // SGMV tiles: (first token or key index, count, adapter, from-keys)
-  std::vector<int32_t> order, tile_order, tiles_sorted;
+  std::vector<int32_t> mb_ad, mb_in, sg_ad, sg_in;  // kept (adapter, token) pairs in token order
+  std::vector<int32_t> mb_tok, sg_tok;  // the same tokens bucketed by adapter (ascending id)
+  std::vector<int32_t> grp;    // MBGMV groups: (index into mb_tok, count, adapter) triples
+  std::vector<int32_t> tiles;  // SGMV tiles: (first token or index into sg_tok, count, adapter, listed)
+  std::vector<int32_t> order, tile_order, tiles_sorted, used, hist;
+  std::vector<int32_t> cnt;    // per adapter; all zero between calls
+  std::vector<uint64_t> bits;
 };
 
 // Validate, group and count; returns the bytes the plan needs, or a negative

@@ -74,7 +74,7 @@ __device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int k0 = it.part * kMbShrinkRows + wave * kRowsPerWave;
   const int nrow = max(0, min(kRowsPerWave, it.rank - k0));  // 0: this wave only stages x
-  const int n = it.n_tok;
+  const int n = it.n_tok();
   const int nvec = g.d_in >> 3;
   const int npid = nrow * g.cA;  // <= 2 * 32 (the planner limits cA)
   const int my_pid = lane < npid ? g.pt[(int64_t)it.pt_base + (int64_t)k0 * g.cA + lane] : -1;
@@ -160,7 +160,7 @@ __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
                                             const void* __restrict__ v, uint16_t* __restrict__ y,
                                             uint32_t tag, unsigned long long* err, float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = it.rank, n = it.n_tok, split = it.split;
+  const int r = it.rank, n = it.n_tok(), split = it.split();
   const int slices = kWaves / split, slice = wave / split, rp = wave % split;
   const int rpw = (r + split - 1) / split;  // rows per wave (<= 32)
   const int k_lo = min(r, rp * rpw), nk = min(r, k_lo + rpw) - k_lo;
@@ -305,15 +305,15 @@ __global__ __launch_bounds__(64 * kWaves) void mbgmv_kernel(
     uint16_t* __restrict__ y, uint32_t tag, unsigned long long* err) {
   extern __shared__ uint4 lds[];  // shrink: [G][kBatchVecs] of x; expand: partial sums
   const MbItem it = items[blockIdx.x];
-  if (it.role == 0) {
-    const int n = it.n_tok;
+  if (it.role() == 0) {
+    const int n = it.n_tok();
     static_assert(kMbGroup == 4, "shrink bodies cover 1, 2 and 4 tokens");
     if (n <= 1) shrink_body<DT, kUniformChunk, 1, kTag>(g, it, x, v, tag, lds);
     else if (n <= 2) shrink_body<DT, kUniformChunk, 2, kTag>(g, it, x, v, tag, lds);
     else shrink_body<DT, kUniformChunk, 4, kTag>(g, it, x, v, tag, lds);
   } else {
     float* red = reinterpret_cast<float*>(lds);
-    if (it.n_tok <= 1) expand_body<DT, kUniformChunk, 1, kTag>(g, it, v, y, tag, err, red);
+    if (it.n_tok() <= 1) expand_body<DT, kUniformChunk, 1, kTag>(g, it, v, y, tag, err, red);
     else expand_body<DT, kUniformChunk, 2, kTag>(g, it, v, y, tag, err, red);
   }
 }

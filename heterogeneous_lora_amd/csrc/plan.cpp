@@ -109,6 +109,74 @@ int32_t n_ctile(const slora_lora* L, int32_t rank) {
   return (L->d_out + cols - 1) / cols;
 }
 
+// Per-adapter counts of the call's kept tokens live in sc->cnt (all zero between calls).
+void clear_counts(PlanScratch* sc) {
+  for (int32_t a : sc->mb_ad) sc->cnt[(size_t)a] = 0;
+  for (int32_t a : sc->sg_ad) sc->cnt[(size_t)a] = 0;
+}
+
+void count_pair(PlanScratch* sc, std::vector<int32_t>* ad, std::vector<int32_t>* in, int32_t a,
+                int32_t t) {
+  ad->push_back(a);
+  in->push_back(t);
+  ++sc->cnt[(size_t)a];
+}
+
+// Counting sort of (adapter, token) pairs by adapter id, tokens kept in input order;
+// appends one record (first, count, adapter[, 1]) per part of at most `cap` tokens
+// (an even split of each adapter's tokens). Leaves the counts of these adapters zero.
+void bucket(PlanScratch* sc, const std::vector<int32_t>& ad, const std::vector<int32_t>& in,
+            std::vector<int32_t>* out_tok, int32_t cap, std::vector<int32_t>* recs, int width) {
+  std::vector<int32_t>& used = sc->used;
+  used.clear();
+  for (int32_t a : ad)
+    if (sc->cnt[(size_t)a] > 0) {
+      used.push_back(a);
+      sc->cnt[(size_t)a] = -sc->cnt[(size_t)a];  // mark as listed
+    }
+  const size_t words = (sc->cnt.size() + 63) / 64;
+  if (used.size() * 16 < words) {
+    std::sort(used.begin(), used.end());
+  } else {  // ascending ids from a bitmap when it is short next to the list
+    sc->bits.assign(words, 0);
+    for (int32_t a : used) sc->bits[(size_t)a >> 6] |= 1ull << (a & 63);
+    used.clear();
+    for (size_t w = 0; w < words; ++w)
+      for (uint64_t b = sc->bits[w]; b; b &= b - 1)
+        used.push_back((int32_t)(w * 64 + (size_t)__builtin_ctzll(b)));
+  }
+  int32_t at = 0;
+  for (int32_t a : used) {
+    const int32_t n = -sc->cnt[(size_t)a];
+    sc->cnt[(size_t)a] = at;  // now the write cursor of a's tokens
+    const Split sp(n, cap);
+    int32_t f = at;
+    for (int32_t p = 0; p < sp.parts; ++p) {
+      recs->push_back(f);
+      recs->push_back(sp.size(p));
+      recs->push_back(a);
+      if (width == 4) recs->push_back(1);  // tile whose tokens come from the list
+      f += sp.size(p);
+    }
+    at += n;
+  }
+  out_tok->resize((size_t)at);
+  for (size_t i = 0; i < ad.size(); ++i) (*out_tok)[(size_t)sc->cnt[(size_t)ad[i]]++] = in[i];
+  for (int32_t a : used) sc->cnt[(size_t)a] = 0;
+}
+
+// Stable order of records (width ints, adapter at index 2) by descending rank.
+void rank_order(const slora_lora* L, const std::vector<int32_t>& recs, int width,
+                std::vector<int32_t>* order, std::vector<int32_t>* hist) {
+  const int32_t n = (int32_t)(recs.size() / (size_t)width);
+  hist->assign(kMaxRank + 2, 0);
+  for (int32_t i = 0; i < n; ++i) ++(*hist)[(size_t)(kMaxRank - L->rank[recs[(size_t)i * width + 2]] + 1)];
+  for (int32_t b = 1; b <= kMaxRank + 1; ++b) (*hist)[(size_t)b] += (*hist)[(size_t)b - 1];
+  order->resize((size_t)n);
+  for (int32_t i = 0; i < n; ++i)
+    (*order)[(size_t)(*hist)[(size_t)(kMaxRank - L->rank[recs[(size_t)i * width + 2]])]++] = i;
+}
+
 }  // namespace
 
 int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc, PlanView* v) {
@@ -117,24 +185,41 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
   if (rc) return rc;
   const int32_t P = L->page_elems;
   const int32_t cA = (L->d_in + P - 1) / P, cB = (L->d_out + P - 1) / P;
-  sc->mb_keys.clear();
-  sc->sg_keys.clear();
+  sc->mb_ad.clear();
+  sc->mb_in.clear();
+  sc->sg_ad.clear();
+  sc->sg_in.clear();
   sc->grp.clear();
   sc->tiles.clear();
+  if ((int64_t)sc->cnt.size() < (int64_t)L->n_adapters) sc->cnt.assign((size_t)L->n_adapters, 0);
   *v = PlanView{};
+  // an adapter is checked when first met in a call (cnt[a] == 0 until a token of it is kept)
+  auto admit = [&](int32_t a) -> int {
+    if (a < -1 || a >= L->n_adapters) {
+      clear_counts(sc);
+      return fail(SLORA_E_INVALID, "adapter id %d outside [-1, %d)", a, L->n_adapters);
+    }
+    if (a < 0) return 0;
+    if (sc->cnt[(size_t)a] > 0) return 1;
+    const int rc = check_adapter(L, a, cA, cB);
+    if (rc < 0) clear_counts(sc);
+    return rc;
+  };
   const int32_t S = R->n_segments;
   for (int32_t s = 0; s < S; ++s) {
     const int32_t b = R->seg_offsets[s], e = R->seg_offsets[s + 1], a = R->seg_adapter[s];
     if (e == b) {  // an empty segment does no work; its id must still be in range
-      if (a < -1 || a >= L->n_adapters)
+      if (a < -1 || a >= L->n_adapters) {
+        clear_counts(sc);
         return fail(SLORA_E_INVALID, "adapter id %d outside [-1, %d)", a, L->n_adapters);
+      }
       continue;
     }
-    rc = check_adapter(L, a, cA, cB);
+    rc = admit(a);
     if (rc < 0) return rc;
     if (rc == 0) continue;
     if (R->policy == SLORA_POLICY_MBGMV) {
-      for (int32_t t = b; t < e; ++t) sc->mb_keys.push_back(((uint64_t)a << 32) | (uint32_t)t);
+      for (int32_t t = b; t < e; ++t) count_pair(sc, &sc->mb_ad, &sc->mb_in, a, t);
     } else {  // a segment's tokens are contiguous: tiles straight from the offsets
       const Split sp(e - b, kSgTile);
       int32_t at = b;
@@ -147,55 +232,27 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
   const int32_t n_dec = R->n_tokens - seg_end;
   for (int32_t q = 0; q < n_dec; ++q) {
     const int32_t a = R->token_adapter[q];
-    rc = check_adapter(L, a, cA, cB);
+    rc = admit(a);
     if (rc < 0) return rc;
     if (rc == 0) continue;
-    const uint64_t key = ((uint64_t)a << 32) | (uint32_t)(seg_end + q);
-    (R->policy == SLORA_POLICY_SGMV ? sc->sg_keys : sc->mb_keys).push_back(key);
+    if (R->policy == SLORA_POLICY_SGMV) count_pair(sc, &sc->sg_ad, &sc->sg_in, a, seg_end + q);
+    else count_pair(sc, &sc->mb_ad, &sc->mb_in, a, seg_end + q);
   }
-  // (adapter, token) keys sort adapter-major with tokens ascending: a stable bucket
-  std::sort(sc->mb_keys.begin(), sc->mb_keys.end());
-  std::sort(sc->sg_keys.begin(), sc->sg_keys.end());
-  auto runs = [](const std::vector<uint64_t>& keys, int32_t cap, std::vector<int32_t>* out,
-                 int32_t width) {
-    for (size_t i = 0; i < keys.size();) {
-      size_t j = i;
-      const uint32_t a = (uint32_t)(keys[i] >> 32);
-      while (j < keys.size() && (uint32_t)(keys[j] >> 32) == a) ++j;
-      const Split sp((int32_t)(j - i), cap);
-      int32_t at = (int32_t)i;
-      for (int32_t p = 0; p < sp.parts; ++p) {
-        out->push_back(at);
-        out->push_back(sp.size(p));
-        out->push_back((int32_t)a);
-        if (width == 4) out->push_back(1);  // tile whose tokens come from the keys
-        at += sp.size(p);
-      }
-      i = j;
-    }
-  };
-  runs(sc->mb_keys, kMbGroup, &sc->grp, 3);
-  runs(sc->sg_keys, kSgTile, &sc->tiles, 4);
+  // tokens bucketed by adapter (ascending id, tokens in ascending order): groups of <= 4
+  // for MBGMV, tiles of <= 64 for SGMV
+  bucket(sc, sc->mb_ad, sc->mb_in, &sc->mb_tok, kMbGroup, &sc->grp, 3);
+  bucket(sc, sc->sg_ad, sc->sg_in, &sc->sg_tok, kSgTile, &sc->tiles, 4);
 
-  // MBGMV groups by descending rank (stable)
+  // groups and tiles by descending rank (stable), the costliest work first
   const int32_t n_groups = (int32_t)(sc->grp.size() / 3);
-  sc->order.resize((size_t)n_groups);
-  for (int32_t gi = 0; gi < n_groups; ++gi) sc->order[(size_t)gi] = gi;
-  std::stable_sort(sc->order.begin(), sc->order.end(), [&](int32_t x, int32_t y) {
-    return L->rank[sc->grp[3 * (size_t)x + 2]] > L->rank[sc->grp[3 * (size_t)y + 2]];
-  });
-  // SGMV tiles by descending rank too (stable: segments first, then bucketed ids)
+  rank_order(L, sc->grp, 3, &sc->order, &sc->hist);
   {
+    rank_order(L, sc->tiles, 4, &sc->tile_order, &sc->hist);
     const size_t nt = sc->tiles.size() / 4;
-    std::vector<int32_t>& idx = sc->tile_order;
-    idx.resize(nt);
-    for (size_t i = 0; i < nt; ++i) idx[i] = (int32_t)i;
-    std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
-      return L->rank[sc->tiles[4 * (size_t)x + 2]] > L->rank[sc->tiles[4 * (size_t)y + 2]];
-    });
     sc->tiles_sorted.resize(sc->tiles.size());
     for (size_t i = 0; i < nt; ++i)
-      for (int j = 0; j < 4; ++j) sc->tiles_sorted[4 * i + j] = sc->tiles[4 * (size_t)idx[i] + j];
+      for (int j = 0; j < 4; ++j)
+        sc->tiles_sorted[4 * i + j] = sc->tiles[4 * (size_t)sc->tile_order[i] + j];
     sc->tiles.swap(sc->tiles_sorted);
   }
   int64_t n_shrink = 0, n_expand = 0;
@@ -214,11 +271,11 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
   v->n_sg = (int32_t)(sc->tiles.size() / 4);
   int32_t sg_tok = 0;
   for (int32_t t = 0; t < v->n_sg; ++t) sg_tok += sc->tiles[4 * (size_t)t + 1];
-  v->n_tok = sg_tok;
-  v->n_routed = (int32_t)sc->mb_keys.size() + sg_tok;
+  v->n_tok = (int32_t)sc->sg_tok.size();  // listed tokens: those of bucketed tiles only
+  v->n_routed = (int32_t)sc->mb_tok.size() + sg_tok;
   return align_up((int64_t)v->n_mb * (int64_t)sizeof(MbItem), 64) +
          align_up((int64_t)v->n_sg * (int64_t)sizeof(SgTile), 64) +
-         align_up((int64_t)sg_tok * 4, 64);
+         align_up((int64_t)v->n_tok * 4, 64);
 }
 
 void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, void* buf,
@@ -231,42 +288,36 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
   p += align_up((int64_t)v->n_sg * (int64_t)sizeof(SgTile), 64);
   v->tok = (int32_t*)p;
 
-  auto base_item = [&](int32_t gi) {
+  // one template per group; items are 32-byte copies of it with `part` (and the token
+  // pair of expand items) filled in
+  MbItem* out = v->mb;
+  MbItem* out_e = v->mb + v->n_mb_shrink;
+  for (int32_t s = 0; s < v->n_groups; ++s) {
+    const int32_t gi = sc->order[(size_t)s];
     const int32_t k0 = sc->grp[3 * (size_t)gi], n = sc->grp[3 * (size_t)gi + 1];
     const int32_t a = sc->grp[3 * (size_t)gi + 2];
-    MbItem it;
+    const int32_t* tk = sc->mb_tok.data() + k0;
+    const int32_t r = L->rank[a];
+    alignas(32) MbItem it;
     memset(&it, 0, sizeof it);
-    for (int32_t t = 0; t < n; ++t) it.tok[t] = (int32_t)(uint32_t)sc->mb_keys[(size_t)(k0 + t)];
-    it.n_tok = n;
+    for (int32_t t = 0; t < n; ++t) it.tok[t] = tk[t];
     it.pt_base = (int32_t)L->base[a];
-    it.rank = L->rank[a];
+    it.rank = (uint8_t)r;
     it.scale = L->scale[a];
-    return it;
-  };
-  MbItem* out = v->mb;
-  for (int32_t s = 0; s < v->n_groups; ++s) {  // shrink items, groups in dispatch order
-    const int32_t gi = sc->order[(size_t)s];
-    MbItem it = base_item(gi);
-    it.role = 0;
-    const int32_t nb = (it.rank + kMbShrinkRows - 1) / kMbShrinkRows;
-    for (int32_t b = 0; b < nb; ++b) {
-      it.part = b;
-      *out++ = it;
+    it.info = MbItem::pack_info(n, 0, 0);
+    const int32_t nb = (r + kMbShrinkRows - 1) / kMbShrinkRows;
+    for (int32_t b = 0; b < nb; ++b, ++out) {  // shrink: role 0, part = row block
+      memcpy(out, &it, sizeof it);
+      out->part = (int16_t)b;
     }
-  }
-  for (int32_t s = 0; s < v->n_groups; ++s) {  // expand items
-    const int32_t gi = sc->order[(size_t)s];
-    const MbItem g = base_item(gi);
-    const int32_t nct = n_ctile(L, g.rank);
-    for (int32_t t0 = 0; t0 < g.n_tok; t0 += kMbExpandTok) {
-      MbItem it = g;
-      it.n_tok = std::min(kMbExpandTok, g.n_tok - t0);
-      for (int32_t t = 0; t < kMbGroup; ++t) it.tok[t] = t < it.n_tok ? g.tok[t0 + t] : 0;
-      it.role = 1;
-      it.split = mb_split(g.rank);
-      for (int32_t ct = 0; ct < nct; ++ct) {
-        it.part = ct;
-        *out++ = it;
+    const int32_t nct = n_ctile(L, r);
+    for (int32_t t0 = 0; t0 < n; t0 += kMbExpandTok) {  // expand: a token pair, part = column tile
+      const int32_t m = std::min(kMbExpandTok, n - t0);
+      it.info = MbItem::pack_info(m, 1, mb_split(r));
+      for (int32_t t = 0; t < kMbGroup; ++t) it.tok[t] = t < m ? tk[t0 + t] : 0;
+      for (int32_t ct = 0; ct < nct; ++ct, ++out_e) {
+        memcpy(out_e, &it, sizeof it);
+        out_e->part = (int16_t)ct;
       }
     }
   }
@@ -284,9 +335,10 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
     tile.first_tok = from_keys ? -1 : first;
     v->sg[t] = tile;
     v->sg_max_rank = std::max(v->sg_max_rank, tile.rank);
-    for (int32_t q = 0; q < n; ++q)
-      v->tok[at + q] = from_keys ? (int32_t)(uint32_t)sc->sg_keys[(size_t)(first + q)] : first + q;
-    at += n;
+    if (from_keys) {  // segment tiles name their tokens by first_tok
+      for (int32_t q = 0; q < n; ++q) v->tok[at + q] = sc->sg_tok[(size_t)(first + q)];
+      at += n;
+    }
   }
 }
 

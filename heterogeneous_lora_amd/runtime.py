@@ -145,6 +145,13 @@ class PagedLoRA:
         s = stream or torch.cuda.current_stream(self.device)
         _lib.apply(call, x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), s.cuda_stream)
 
+    def bind_apply(self, call: _lib.Call, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
+                   stream: Optional[torch.cuda.Stream] = None):
+        """apply() with its arguments marshalled once (a callable with no arguments)."""
+        s = stream or torch.cuda.current_stream(self.device)
+        return _lib.bind_apply(call, x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(),
+                               s.cuda_stream)
+
     def shrink(self, call, x, v, ws, stream=None):
         s = stream or torch.cuda.current_stream(self.device)
         _lib.shrink(call, x.data_ptr(), v.data_ptr(), ws.data_ptr(), ws.numel(), s.cuda_stream)

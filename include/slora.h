@@ -201,7 +201,8 @@ int slora_workspace_status(const void* ws, void* stream, int32_t* status);
 
 /* Kernel timing for benchmarks. While enabled (on != 0), every kernel a compute
  * call launches is bracketed by two HIP events recorded on the call's stream.
- * Enabling clears the counters. Kernel ids: SLORA_K_MBGMV_SHRINK,
+ * Recorded launches accumulate across enable / disable until slora_timing_read
+ * returns and clears them, so a caller can time a sample of its calls. Kernel ids: SLORA_K_MBGMV_SHRINK,
  * SLORA_K_MBGMV_EXPAND, SLORA_K_SGMV_SHRINK, SLORA_K_SGMV_EXPAND, SLORA_K_MBGMV_FUSED (the decode
  * shrink and expand in one launch, as slora_apply runs them). */
 #define SLORA_K_MBGMV_SHRINK 0
