@@ -102,11 +102,14 @@ def load_traffic(kernel, workload):
 
 
 def calib_copy(nbytes, reps):
-    """A plain device-to-device copy of known size (the reference the byte counters are
-    scaled by): `reps` launches of torch's copy kernel over nbytes."""
+    """Plain copies of known size, the reference the byte counters are scaled by: `reps`
+    launches of torch's elementwise kernel computing dst = src * 1 over nbytes (ordinary
+    loads and stores), then `reps` device-to-device copies (the runtime's copy kernel)."""
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
     for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
