@@ -24,6 +24,7 @@ constexpr int kMbExpandTok = 2;     // MBGMV expand: tokens per workgroup
 constexpr int kMbWaveCols = 512;    // MBGMV expand: output columns per wave (64 lanes x 8)
 constexpr int kMbRowsPerWave = 16;  // MBGMV expand: B rows a wave keeps in flight
 constexpr int kSgTile = 64;         // SGMV: tokens per tile
+constexpr int kXcds = 8;            // XCDs (dies, each with its own L2) workgroups are dealt to in turn
 constexpr int kSgMaxSplit = 8;      // SGMV shrink: most k-ranges d_in is cut into
 
 // k-ranges the SGMV shrink may cut d_in into (each at least 256 long).

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
   constexpr int kRp = KB * kStep;     // padded rank
   constexpr int kVPitch = kRp + 8;    // v row pitch in elements
   __shared__ uint16_t vs[kTileRows * kVPitch];
-  __shared__ uint16_t bs[kChunkRows * kBPitch];
+  __shared__ uint16_t bs[KB * kChunkRows * kBPitch];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
   const SgTile tl = tiles[blockIdx.x];
@@ -210,35 +210,53 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) tk[tb] = tile_token(tl, tok, tb * 16 + li);
 
-  // B staging: thread -> column slot (8 columns) and rows row0 + 16 i of a chunk
+  // B staging: thread -> column slot (8 columns) and rows ch * 32 + row0 + 16 i of every
+  // chunk. A pass's rows are loaded in one go, a pass ahead; the page ids of the
+  // thread's rows are kept while the pass's columns stay in the same page chunk.
   constexpr int kSlots = kCols / 8, kRowStep = 64 * kWaves / kSlots, kBLoads = kChunkRows / kRowStep;
   const int slot = tid % kSlots, row0 = tid / kSlots;
-  auto load_b = [&](uint4 (&b)[kBLoads], int j) {  // chunk j % KB of pass j / KB
-    const int bcol = col_begin + (j / KB) * kCols + slot * 8;
+  int pid_c = -1;
+  int pids[KB][kBLoads];
+  auto load_b = [&](uint4 (&b)[KB][kBLoads], int pass) {
+    const int bcol = col_begin + pass * kCols + slot * 8;
     const bool live = bcol < g.d_out;
     const int bc = live ? bcol / g.P : 0;
-    const int64_t bbase = (int64_t)tl.pt_base + (int64_t)r * g.cA + bc;
+    if (live && bc != pid_c) {
+      const int64_t bbase = (int64_t)tl.pt_base + (int64_t)r * g.cA + bc;
 #pragma unroll
-    for (int i = 0; i < kBLoads; ++i) {
-      const int kr = (j % KB) * kChunkRows + row0 + i * kRowStep;
-      const uint16_t* p = fill_zero();
-      if (live && kr < r) {
-        const int page = g.pt[bbase + (int64_t)kr * g.cB];
-        p = (uint32_t)page < (uint64_t)g.n_pages ? g.pool + (int64_t)page * g.P + (bcol - bc * g.P)
-                                                 : fill_nan<DT>();
+      for (int ch = 0; ch < KB; ++ch)
+#pragma unroll
+        for (int i = 0; i < kBLoads; ++i) {
+          const int kr = ch * kChunkRows + row0 + i * kRowStep;
+          pids[ch][i] = kr < r ? g.pt[bbase + (int64_t)kr * g.cB] : -1;
+        }
+      pid_c = bc;
+    }
+#pragma unroll
+    for (int ch = 0; ch < KB; ++ch)
+#pragma unroll
+      for (int i = 0; i < kBLoads; ++i) {
+        const int kr = ch * kChunkRows + row0 + i * kRowStep;
+        const uint16_t* p = fill_zero();
+        if (live && kr < r) {
+          const int page = pids[ch][i];
+          p = (uint32_t)page < (uint64_t)g.n_pages ? g.pool + (int64_t)page * g.P + (bcol - bc * g.P)
+                                                   : fill_nan<DT>();
+        }
+        b[ch][i] = ld16(p);
       }
-      b[i] = ld16(p);
-    }
   };
-  auto store_b = [&](const uint4 (&b)[kBLoads]) {
+  auto store_b = [&](const uint4 (&b)[KB][kBLoads]) {
 #pragma unroll
-    for (int i = 0; i < kBLoads; ++i) {
-      uint2* d = reinterpret_cast<uint2*>(&bs[(row0 + i * kRowStep) * kBPitch + slot * 8]);
-      d[0] = make_uint2(b[i].x, b[i].y);
-      d[1] = make_uint2(b[i].z, b[i].w);
-    }
+    for (int ch = 0; ch < KB; ++ch)
+#pragma unroll
+      for (int i = 0; i < kBLoads; ++i) {
+        uint2* d = reinterpret_cast<uint2*>(&bs[(ch * kChunkRows + row0 + i * kRowStep) * kBPitch + slot * 8]);
+        d[0] = make_uint2(b[ch][i].x, b[ch][i].y);
+        d[1] = make_uint2(b[ch][i].z, b[ch][i].w);
+      }
   };
-  uint4 bn[kBLoads];
+  uint4 bn[KB][kBLoads];
   load_b(bn, 0);  // in flight while v is staged
 
   // v: the k-range partials added in range order, rounded once, into LDS. Thread:
@@ -283,7 +301,6 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
   }
 
   const float s = tl.scale;
-  const int n_j = n_pass * KB;
   // y0 of this lane's outputs in a pass: token tk[tb], columns cw + kg * 8 + [0, 8)
   auto load_y0 = [&](uint4 (&yv)[4], int pass) {
     const int col = col_begin + pass * kCols + wave * 32 + kg * 8;
@@ -297,13 +314,13 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[h][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // v is staged / the previous pass's rows have been read
+    store_b(bn);
+    if (pass + 1 < n_pass) load_b(bn, pass + 1);
+    __syncthreads();
 #pragma unroll
     for (int ch = 0; ch < KB; ++ch) {
-      const int j = pass * KB + ch;
-      __syncthreads();  // v is staged / the previous chunk has been read
-      store_b(bn);
-      if (j + 1 < n_j) load_b(bn, j + 1);
-      __syncthreads();
+      const uint16_t* bsc = bs + ch * kChunkRows * kBPitch;
       // v^T operand: token tb * 16 + li, k = ch * 32 + kg * 8 + [0, 8)
       uint4 vo[4];
 #pragma unroll
@@ -314,7 +331,7 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int colw = wave * 32 + (li >> 2) * 8 + h * 4 + (li & 3);
-        const uint16_t* src = &bs[(kg * 8) * kBPitch + colw];
+        const uint16_t* src = &bsc[(kg * 8) * kBPitch + colw];
         uint4 bo;
         bo.x = (uint32_t)src[0 * kBPitch] | ((uint32_t)src[1 * kBPitch] << 16);
         bo.y = (uint32_t)src[2 * kBPitch] | ((uint32_t)src[3 * kBPitch] << 16);
