@@ -198,6 +198,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_7b")
     ap.add_argument("--policy", default="auto", choices=["auto", "mbgmv", "sgmv"])
+    ap.add_argument("--active", type=int, default=0,
+                    help="mlp_asym only: number of active adapters (tokens per adapter = 4096 / this)")
     ap.add_argument("--instances", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -230,7 +232,7 @@ def main():
 
     _lib.load()
     policy = {"auto": 0, "mbgmv": 1, "sgmv": 2}[args.policy]
-    wl = workloads.make(args.config)
+    wl = workloads.make(args.config, **({"n_active": args.active} if args.active else {}))
     T = wl.n_tokens
     n_proj = len(wl.projections)
     dev = torch.device("cuda:0")

@@ -24,6 +24,8 @@ constexpr int kMbExpandTok = 2;     // MBGMV expand: tokens per workgroup
 constexpr int kMbWaveCols = 512;    // MBGMV expand: output columns per wave (64 lanes x 8)
 constexpr int kMbRowsPerWave = 16;  // MBGMV expand: B rows a wave keeps in flight
 constexpr int kSgTile = 64;         // SGMV: tokens per tile
+constexpr int kAutoSgmvTok = 4;     // AUTO: an adapter's per-token ids go to SGMV from this many
+constexpr int kAutoSgmvBatch = 256; // AUTO: ... when at least this many such tokens (or segments run)
 constexpr int kXcds = 8;            // XCDs (dies, each with its own L2) workgroups are dealt to in turn
 constexpr int kSgMaxSplit = 8;      // SGMV shrink: most k-ranges d_in is cut into
 
@@ -103,7 +105,7 @@ struct PlanScratch {
   std::vector<int32_t> mb_tok, sg_tok;  // the same tokens bucketed by adapter (ascending id)
   std::vector<int32_t> grp;    // MBGMV groups: (index into mb_tok, count, adapter) triples
   std::vector<int32_t> tiles;  // SGMV tiles: (first token or index into sg_tok, count, adapter, listed)
-  std::vector<int32_t> order, tile_order, tiles_sorted, used, hist;
+  std::vector<int32_t> order, tile_order, tiles_sorted, used, hist, seen;
   std::vector<int32_t> cnt;    // per adapter; all zero between calls
   std::vector<uint64_t> bits;
 };

@@ -113,6 +113,7 @@ int32_t n_ctile(const slora_lora* L, int32_t rank) {
 void clear_counts(PlanScratch* sc) {
   for (int32_t a : sc->mb_ad) sc->cnt[(size_t)a] = 0;
   for (int32_t a : sc->sg_ad) sc->cnt[(size_t)a] = 0;
+  for (int32_t a : sc->seen) sc->cnt[(size_t)a] = 0;
 }
 
 void count_pair(PlanScratch* sc, std::vector<int32_t>* ad, std::vector<int32_t>* in, int32_t a,
@@ -187,6 +188,7 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
   const int32_t cA = (L->d_in + P - 1) / P, cB = (L->d_out + P - 1) / P;
   sc->mb_ad.clear();
   sc->mb_in.clear();
+  sc->seen.clear();
   sc->sg_ad.clear();
   sc->sg_in.clear();
   sc->grp.clear();
@@ -230,13 +232,38 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
     }
   }
   const int32_t n_dec = R->n_tokens - seg_end;
-  for (int32_t q = 0; q < n_dec; ++q) {
-    const int32_t a = R->token_adapter[q];
-    rc = admit(a);
-    if (rc < 0) return rc;
-    if (rc == 0) continue;
-    if (R->policy == SLORA_POLICY_SGMV) count_pair(sc, &sc->sg_ad, &sc->sg_in, a, seg_end + q);
-    else count_pair(sc, &sc->mb_ad, &sc->mb_in, a, seg_end + q);
+  if (R->policy == SLORA_POLICY_AUTO) {
+    // Per-token ids of an adapter with at least kAutoSgmvTok tokens in the call go to
+    // SGMV tiles (its weights are then read once per 64 tokens instead of once per 4)
+    // when SGMV runs anyway (segments) or when they are numerous enough to pay for its
+    // launches (kAutoSgmvBatch tokens); the rest to MBGMV.
+    for (int32_t q = 0; q < n_dec; ++q) {
+      const int32_t a = R->token_adapter[q];
+      rc = admit(a);
+      if (rc < 0) return rc;
+      if (rc == 0) continue;
+      if (sc->cnt[(size_t)a]++ == 0) sc->seen.push_back(a);
+    }
+    int64_t hot = 0;
+    for (int32_t a : sc->seen)
+      if (sc->cnt[(size_t)a] >= kAutoSgmvTok) hot += sc->cnt[(size_t)a];
+    const bool sg_hot = hot > 0 && (!sc->tiles.empty() || hot >= kAutoSgmvBatch);
+    for (int32_t q = 0; q < n_dec; ++q) {
+      const int32_t a = R->token_adapter[q];
+      if (a < 0 || sc->cnt[(size_t)a] == 0) continue;  // no adapter, or rank 0
+      const bool to_sg = sg_hot && sc->cnt[(size_t)a] >= kAutoSgmvTok;
+      (to_sg ? sc->sg_ad : sc->mb_ad).push_back(a);
+      (to_sg ? sc->sg_in : sc->mb_in).push_back(seg_end + q);
+    }
+  } else {
+    for (int32_t q = 0; q < n_dec; ++q) {
+      const int32_t a = R->token_adapter[q];
+      rc = admit(a);
+      if (rc < 0) return rc;
+      if (rc == 0) continue;
+      if (R->policy == SLORA_POLICY_SGMV) count_pair(sc, &sc->sg_ad, &sc->sg_in, a, seg_end + q);
+      else count_pair(sc, &sc->mb_ad, &sc->mb_in, a, seg_end + q);
+    }
   }
   // tokens bucketed by adapter (ascending id, tokens in ascending order): groups of <= 4
   // for MBGMV, tiles of <= 64 for SGMV

@@ -291,7 +291,7 @@ def test_fetch_waits_and_free_state(rt):
 
 
 LARGE = [("mixed_13b", 1), ("mlp_asym", 1), ("prefill_sgmv", 0), ("mixed_13b", 0),
-         ("mlp_asym", 2)]
+         ("mlp_asym", 2), ("mlp_asym", 0)]
 
 
 @pytest.mark.timeout(900)

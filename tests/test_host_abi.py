@@ -181,6 +181,7 @@ def test_validation_rejects_bad_calls():
 # ------------------------------------------------------------------ planner vs Python model
 
 MB_GROUP, SG_TILE = 4, 64
+AUTO_SGMV_TOK, AUTO_SGMV_BATCH = 4, 256
 
 
 def _even_split(toks, cap):
@@ -210,11 +211,20 @@ def model_plan(wl, base, policy):
             mb += [(a, t) for t in toks]
         else:
             sg += [(a, c) for c in _even_split(toks, SG_TILE)]
-    for q, a in enumerate(ta):
-        a = int(a)
-        if not live(a):
-            continue
-        (sg_ids if policy == _lib.POLICY_SGMV else mb).append((a, seg_end + q))
+    dec = [(int(a), seg_end + q) for q, a in enumerate(ta) if live(int(a))]
+    if policy == _lib.POLICY_AUTO:
+        # an adapter's per-token ids go to SGMV from AUTO_SGMV_TOK of them, when segments run
+        # anyway or there are at least AUTO_SGMV_BATCH such tokens
+        cnt = {}
+        for a, _ in dec:
+            cnt[a] = cnt.get(a, 0) + 1
+        hot = sum(c for c in cnt.values() if c >= AUTO_SGMV_TOK)
+        sg_hot = hot > 0 and (len(sg) > 0 or hot >= AUTO_SGMV_BATCH)
+        for a, t in dec:
+            (sg_ids if sg_hot and cnt[a] >= AUTO_SGMV_TOK else mb).append((a, t))
+    else:
+        for a, t in dec:
+            (sg_ids if policy == _lib.POLICY_SGMV else mb).append((a, t))
     def buckets(pairs, cap):
         pairs = sorted(pairs, key=lambda p: p[0])  # stable
         out = []
@@ -234,7 +244,7 @@ def model_plan(wl, base, policy):
     ("tiny_decode", _lib.POLICY_AUTO), ("decode_7b", _lib.POLICY_AUTO),
     ("decode_7b", _lib.POLICY_SGMV), ("mixed_13b", _lib.POLICY_AUTO),
     ("mixed_13b", _lib.POLICY_MBGMV), ("mixed_13b", _lib.POLICY_SGMV),
-    ("prefill_sgmv", _lib.POLICY_AUTO), ("random", _lib.POLICY_AUTO),
+    ("prefill_sgmv", _lib.POLICY_AUTO), ("mlp_asym", _lib.POLICY_AUTO), ("random", _lib.POLICY_AUTO),
     ("random", _lib.POLICY_MBGMV), ("random", _lib.POLICY_SGMV)])
 def test_plan_matches_model(wl_name, policy):
     if wl_name == "random":

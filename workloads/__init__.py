@@ -232,9 +232,12 @@ def mlp(seed: int = 0, n_active: int = 500) -> Workload:
     tok = _rng(seed, _ROUTING, n_active).integers(0, n_active, size=4096).astype(np.int32)
     projs = [Projection("gate", 4096, 11008), Projection("up", 4096, 11008),
              Projection("down", 11008, 4096)]
+    # 524,288 pages hold 500 adapters' pages with room for KV; more adapters get a
+    # proportionally larger pool (a multiple of 65,536 pages)
+    n_pages = 524288 if n_active <= 500 else -(-int(n_active / 500 * 1.15 * 524288) // 65536) * 65536
     return Workload(
         name="mlp_asym" if n_active == 500 else f"mlp_asym_a{n_active}", dtype="bf16",
-        page_elems=4096, n_pages=524288, projections=projs, n_adapters=n_active,
+        page_elems=4096, n_pages=n_pages, projections=projs, n_adapters=n_active,
         ranks=ranks, scales=_scales(ranks), seg_offsets=np.zeros(1, np.int32),
         seg_adapter=np.zeros(0, np.int32), token_adapter=tok,
         kv_seq_lens=np.zeros(0, np.int32), seed=seed, pool_seed=seed,
