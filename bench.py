@@ -335,7 +335,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "kernel_timing": f"HIP events on the launch stream around every kernel of 1 step in {ev}",
+        "kernel_timing": f"HIP events recorded by the launch at kernel start and end, on the launch "
+                         f"stream, for every kernel of 1 step in {ev}",
         "step_kernel_us": round(kern_total_s * 1e6, 2),
         "step_algorithmic_gbps": round(step_bytes / kern_total_s / 1e9, 1),
         "fetch": {"bytes": fetch_bytes, "ms": round(float(np.median(fetch_ms)), 3),

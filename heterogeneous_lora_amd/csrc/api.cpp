@@ -66,7 +66,8 @@ int acquire_slot(size_t n, StagingSlot** out) {
   return SLORA_OK;
 }
 
-// Kernel timing: event pairs around launches while enabled (benchmarks only).
+// Kernel timing while enabled (benchmarks only): each timed launch is given an event
+// pair that the launch itself records at the kernel's start and end.
 struct TimedLaunch {
   int kernel;
   hipEvent_t start, stop;
@@ -77,7 +78,7 @@ std::vector<std::pair<hipEvent_t, hipEvent_t>> g_spare_events;
 
 template <typename F>
 hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
-  if (!g_timing_on) return launch();
+  if (!g_timing_on) return launch(LaunchEvents());
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   if (!g_spare_events.empty()) {
     ev = g_spare_events.back();
@@ -88,9 +89,10 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
     e = hipEventCreate(&ev.second);
     if (e != hipSuccess) { (void)hipEventDestroy(ev.first); return e; }
   }
-  hipError_t e = hipEventRecord(ev.first, s);
-  if (e == hipSuccess) e = launch();
-  if (e == hipSuccess) e = hipEventRecord(ev.second, s);
+  LaunchEvents le;
+  le.start = ev.first;
+  le.stop = ev.second;
+  const hipError_t e = launch(le);
   if (e != hipSuccess) {
     g_spare_events.push_back(ev);
     return e;
@@ -173,16 +175,16 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
     }
     const int64_t stride = (int64_t)R->n_tokens * v_stride;
     if (mode & kShrink) {
-      e = timed_launch(SLORA_K_SGMV_SHRINK, s, [&] {
+      e = timed_launch(SLORA_K_SGMV_SHRINK, s, [&](const LaunchEvents& le) {
         return launch_sgmv_shrink(g, pv.tok, pv.sg, pv.n_sg, pv.sg_max_rank, sp.ksplit, sp.kc, x,
-                                  vpart, v_stride, stride, s);
+                                  vpart, v_stride, stride, s, le);
       });
       if (e != hipSuccess) return hip_fail(e, "sgmv_shrink launch");
     }
     if (mode & kExpand) {
-      e = timed_launch(SLORA_K_SGMV_EXPAND, s, [&] {
+      e = timed_launch(SLORA_K_SGMV_EXPAND, s, [&](const LaunchEvents& le) {
         return launch_sgmv_expand(g, pv.tok, pv.sg, pv.n_sg, pv.sg_max_rank, sp.ksplit, vpart,
-                                  v_stride, stride, y, s);
+                                  v_stride, stride, y, s, le);
       });
       if (e != hipSuccess) return hip_fail(e, "sgmv_expand launch");
     }
@@ -190,19 +192,19 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
   if (pv.n_mb) {
     const bool has_expand = pv.n_mb > pv.n_mb_shrink;
     if (mode == kApply) {
-      e = timed_launch(SLORA_K_MBGMV_FUSED, s, [&] {
+      e = timed_launch(SLORA_K_MBGMV_FUSED, s, [&](const LaunchEvents& le) {
         return launch_mbgmv(g, pv.mb, pv.n_mb, pv.n_mb_shrink > 0, has_expand, pv.mb_max_tok, x,
-                            v, y, tag, err, s);
+                            v, y, tag, err, s, le);
       });
     } else if (mode == kShrink) {
-      e = timed_launch(SLORA_K_MBGMV_SHRINK, s, [&] {
+      e = timed_launch(SLORA_K_MBGMV_SHRINK, s, [&](const LaunchEvents& le) {
         return launch_mbgmv(g, pv.mb, pv.n_mb_shrink, true, false, pv.mb_max_tok, x, v, nullptr, 0,
-                            err, s);
+                            err, s, le);
       });
     } else {
-      e = timed_launch(SLORA_K_MBGMV_EXPAND, s, [&] {
+      e = timed_launch(SLORA_K_MBGMV_EXPAND, s, [&](const LaunchEvents& le) {
         return launch_mbgmv(g, pv.mb + pv.n_mb_shrink, pv.n_mb - pv.n_mb_shrink, false, true,
-                            pv.mb_max_tok, nullptr, const_cast<float*>(vr), y, 0, err, s);
+                            pv.mb_max_tok, nullptr, const_cast<float*>(vr), y, 0, err, s, le);
       });
     }
     if (e != hipSuccess) return hip_fail(e, "mbgmv launch");

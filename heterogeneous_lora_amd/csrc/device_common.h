@@ -2,6 +2,7 @@
 // dot products, 16-byte loads and the wave-wide transposing reduction.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -128,12 +128,18 @@ struct WsLayout {
 WsLayout ws_layout(const slora_lora* L, const slora_routing* R);
 
 // ---------------------------------------------------------------- launchers
+// Optional HIP events that the launch itself records at the kernel's start and end
+// (hipExtLaunchKernel), so a timed interval holds the kernel and nothing else.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
 // One launch over items (role per item; `shrinks` / `expands` say which roles
 // occur). tag != 0 makes it a fused apply: v is the workspace's tagged words,
 // shrink items write them and expand items poll them. tag == 0: v is plain fp32.
 hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
                         bool expands, int32_t max_tok, const void* x, void* v, void* y,
-                        uint32_t tag, unsigned long long* err, hipStream_t s);
+                        uint32_t tag, unsigned long long* err, hipStream_t s,
+                        const LaunchEvents& ev = LaunchEvents());
 // Zero `bytes` (a multiple of 16) of device memory with a kernel.
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s);
 // SGMV shrink over ksplit (<= kSgMaxSplit) k-ranges of kc (a multiple of 128)
@@ -146,11 +152,11 @@ SgSplit sg_split(int32_t d_in, int32_t n_tiles);
 hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
                               const void* x, float* vpart, int32_t v_stride, int64_t split_stride,
-                              hipStream_t s);
+                              hipStream_t s, const LaunchEvents& ev = LaunchEvents());
 hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, int32_t max_rank, int32_t ksplit,
                               const float* vpart, int32_t v_stride, int64_t split_stride, void* y,
-                              hipStream_t s);
+                              hipStream_t s, const LaunchEvents& ev = LaunchEvents());
 
 constexpr int kFetchMaxPages = 240;
 struct FetchArgs {

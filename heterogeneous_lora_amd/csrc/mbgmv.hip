@@ -321,16 +321,16 @@ __global__ __launch_bounds__(64 * kWaves) void mbgmv_kernel(
 template <int DT, bool kTag>
 hipError_t launch_dt(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
                      bool expands, int32_t g_max, const void* x, void* v, void* y, uint32_t tag,
-                     unsigned long long* err, hipStream_t s) {
+                     unsigned long long* err, hipStream_t s, const LaunchEvents& ev) {
   const dim3 grid((unsigned)n_items), block(64 * kWaves);
   size_t lds = shrinks ? (size_t)g_max * kBatchVecs * sizeof(uint4) : 0;
   if (expands) lds = lds > (size_t)kRedBytes ? lds : (size_t)kRedBytes;
   if (g.P % 512 == 0)
-    hipLaunchKernelGGL((mbgmv_kernel<DT, true, kTag>), grid, block, lds, s, g, items,
-                       (const uint16_t*)x, v, (uint16_t*)y, tag, err);
+    hipExtLaunchKernelGGL((mbgmv_kernel<DT, true, kTag>), grid, block, lds, s, ev.start, ev.stop, 0,
+                          g, items, (const uint16_t*)x, v, (uint16_t*)y, tag, err);
   else
-    hipLaunchKernelGGL((mbgmv_kernel<DT, false, kTag>), grid, block, lds, s, g, items,
-                       (const uint16_t*)x, v, (uint16_t*)y, tag, err);
+    hipExtLaunchKernelGGL((mbgmv_kernel<DT, false, kTag>), grid, block, lds, s, ev.start, ev.stop, 0,
+                          g, items, (const uint16_t*)x, v, (uint16_t*)y, tag, err);
   return hipGetLastError();
 }
 
@@ -343,17 +343,17 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n) {
 
 hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
                         bool expands, int32_t max_tok, const void* x, void* v, void* y,
-                        uint32_t tag, unsigned long long* err, hipStream_t s) {
+                        uint32_t tag, unsigned long long* err, hipStream_t s, const LaunchEvents& ev) {
   if (n_items <= 0) return hipSuccess;
   if (max_tok < 1 || max_tok > kMbGroup) return hipErrorInvalidValue;
   const int g_max = max_tok <= 1 ? 1 : max_tok <= 2 ? 2 : 4;
   if (tag)
     return g.dtype == SLORA_F16
-               ? launch_dt<SLORA_F16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, s)
-               : launch_dt<SLORA_BF16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, s);
+               ? launch_dt<SLORA_F16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, s, ev)
+               : launch_dt<SLORA_BF16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, s, ev);
   return g.dtype == SLORA_F16
-             ? launch_dt<SLORA_F16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, s)
-             : launch_dt<SLORA_BF16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, s);
+             ? launch_dt<SLORA_F16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, s, ev)
+             : launch_dt<SLORA_BF16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, s, ev);
 }
 
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s) {

@@ -372,15 +372,15 @@ __global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
 template <int DT>
 hipError_t shrink_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
                      int32_t ksplit, int32_t kc, int32_t nb, const void* x, float* vpart,
-                     int32_t v_stride, int64_t split_stride, hipStream_t s) {
+                     int32_t v_stride, int64_t split_stride, hipStream_t s, const LaunchEvents& ev) {
   const dim3 grid((unsigned)n_tiles, (unsigned)ksplit), block(64 * kWaves);
   const size_t lds = 0;
   const uint16_t* xp = (const uint16_t*)x;
   switch (nb) {
-    case 1: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 1>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
-    case 2: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 2>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
-    case 4: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 4>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
-    default: hipLaunchKernelGGL((sgmv_shrink_kernel<DT, 8>), grid, block, lds, s, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
+    case 1: hipExtLaunchKernelGGL((sgmv_shrink_kernel<DT, 1>), grid, block, lds, s, ev.start, ev.stop, 0, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
+    case 2: hipExtLaunchKernelGGL((sgmv_shrink_kernel<DT, 2>), grid, block, lds, s, ev.start, ev.stop, 0, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
+    case 4: hipExtLaunchKernelGGL((sgmv_shrink_kernel<DT, 4>), grid, block, lds, s, ev.start, ev.stop, 0, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
+    default: hipExtLaunchKernelGGL((sgmv_shrink_kernel<DT, 8>), grid, block, lds, s, ev.start, ev.stop, 0, g, tiles, tok, kc, xp, vpart, v_stride, split_stride); break;
   }
   return hipGetLastError();
 }
@@ -388,14 +388,14 @@ hipError_t shrink_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int
 template <int DT>
 hipError_t expand_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
                      int32_t ksplit, int32_t kb, const float* vpart, int32_t v_stride,
-                     int64_t split_stride, void* y, hipStream_t s) {
+                     int64_t split_stride, void* y, hipStream_t s, const LaunchEvents& ev) {
   const int per_wg = kSubPasses * kCols;
   const dim3 grid((unsigned)n_tiles, (unsigned)((g.d_out + per_wg - 1) / per_wg)), block(64 * kWaves);
   uint16_t* yp = (uint16_t*)y;
   switch (kb) {
-    case 1: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 1>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
-    case 2: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 2>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
-    default: hipLaunchKernelGGL((sgmv_expand_kernel<DT, 4>), grid, block, 0, s, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
+    case 1: hipExtLaunchKernelGGL((sgmv_expand_kernel<DT, 1>), grid, block, 0, s, ev.start, ev.stop, 0, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
+    case 2: hipExtLaunchKernelGGL((sgmv_expand_kernel<DT, 2>), grid, block, 0, s, ev.start, ev.stop, 0, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
+    default: hipExtLaunchKernelGGL((sgmv_expand_kernel<DT, 4>), grid, block, 0, s, ev.start, ev.stop, 0, g, tiles, tok, ksplit, vpart, v_stride, split_stride, yp); break;
   }
   return hipGetLastError();
 }
@@ -415,27 +415,27 @@ SgSplit sg_split(int32_t d_in, int32_t n_tiles) {
 hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
                               const void* x, float* vpart, int32_t v_stride, int64_t split_stride,
-                              hipStream_t s) {
+                              hipStream_t s, const LaunchEvents& ev) {
   if (n_tiles <= 0) return hipSuccess;
   if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit || kc % kRound)
     return hipErrorInvalidValue;
   const int nb = max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8;
   return g.dtype == SLORA_F16
-             ? shrink_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, v_stride, split_stride, s)
-             : shrink_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, v_stride, split_stride, s);
+             ? shrink_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, v_stride, split_stride, s, ev)
+             : shrink_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, v_stride, split_stride, s, ev);
 }
 
 hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* tiles,
                               int32_t n_tiles, int32_t max_rank, int32_t ksplit,
                               const float* vpart, int32_t v_stride, int64_t split_stride, void* y,
-                              hipStream_t s) {
+                              hipStream_t s, const LaunchEvents& ev) {
   if (n_tiles <= 0) return hipSuccess;
   if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit)
     return hipErrorInvalidValue;
   const int kb = max_rank <= 32 ? 1 : max_rank <= 64 ? 2 : 4;
   return g.dtype == SLORA_F16
-             ? expand_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kb, vpart, v_stride, split_stride, y, s)
-             : expand_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kb, vpart, v_stride, split_stride, y, s);
+             ? expand_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kb, vpart, v_stride, split_stride, y, s, ev)
+             : expand_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kb, vpart, v_stride, split_stride, y, s, ev);
 }
 
 }  // namespace slora

@@ -200,7 +200,9 @@ int slora_apply(const slora_lora* lora, const slora_routing* routing, const void
 int slora_workspace_status(const void* ws, void* stream, int32_t* status);
 
 /* Kernel timing for benchmarks. While enabled (on != 0), every kernel a compute
- * call launches is bracketed by two HIP events recorded on the call's stream.
+ * call launches carries two HIP events that the launch itself records on the call's
+ * stream when the kernel starts and when it ends (hipExtLaunchKernel), so a timed
+ * interval spans the kernel alone.
  * Recorded launches accumulate across enable / disable until slora_timing_read
  * returns and clears them, so a caller can time a sample of its calls. Kernel ids: SLORA_K_MBGMV_SHRINK,
  * SLORA_K_MBGMV_EXPAND, SLORA_K_SGMV_SHRINK, SLORA_K_SGMV_EXPAND, SLORA_K_MBGMV_FUSED (the decode
