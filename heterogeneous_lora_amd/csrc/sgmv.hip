@@ -70,8 +70,16 @@ __device__ __forceinline__ int tile_token(const SgTile& tl, const int32_t* tok, 
 constexpr int kBatch = 4 * kStep;  // k per batch
 constexpr int kSegs = kBatch / 8;  // 16-byte segments per slab row
 
+// Waves per SIMD the register allocation must leave room for. Left to itself the
+// compiler spreads these kernels over the unified register file (accumulation
+// registers included) and lands at 3 (shrink, NB = 4) or 2 (expand, KB = 2) waves per
+// SIMD; the same code fits 4 and 3 without spilling, and the extra resident waves
+// keep more loads in flight.
+constexpr int shrink_waves(int nb) { return nb <= 4 ? 4 : 1; }
+constexpr int expand_waves(int kb) { return kb <= 1 ? 4 : kb <= 2 ? 3 : 1; }
+
 template <int DT, int NB>
-__global__ __launch_bounds__(64 * kWaves) void sgmv_shrink_kernel(
+__global__ __launch_bounds__(64 * kWaves, shrink_waves(NB)) void sgmv_shrink_kernel(
     Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t kc,
     const uint16_t* __restrict__ x, float* __restrict__ vpart, int32_t v_stride,
     int64_t split_stride) {
@@ -191,7 +199,7 @@ constexpr int kChunkRows = kStep;          // B rows staged per chunk
 
 // KB: 32-row chunks of the rank (rank <= 32 * KB).
 template <int DT, int KB>
-__global__ __launch_bounds__(64 * kWaves) void sgmv_expand_kernel(
+__global__ __launch_bounds__(64 * kWaves, expand_waves(KB)) void sgmv_expand_kernel(
     Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t ksplit,
     const float* __restrict__ vpart, int32_t v_stride, int64_t split_stride,
     uint16_t* __restrict__ y) {
