@@ -18,17 +18,28 @@ using namespace slora;
 
 namespace {
 
-// Pinned staging ring. A slot is written by the host only after the kernels that
-// read the previous plan in it have finished (its event).
+// Pinned staging ring. The host writes a slot only after the kernels that read its
+// previous plan have finished. Slots are guarded in groups of kGroup consecutive
+// calls: one event, recorded after the group's last call, covers the group when all
+// its calls went to one stream (an event per call puts a marker packet behind every
+// launch, ~3 us of GPU time per decode call). A group whose calls went to more than
+// one stream, or one of whose calls failed after taking its slot, is waited for with
+// a device synchronization when its slots come round again.
 struct StagingSlot {
   void* host = nullptr;
   size_t cap = 0;
-  hipEvent_t ev = nullptr;
-  bool pending = false;
 };
 constexpr int kSlots = 16;
+constexpr int kGroup = 8;
+struct SlotGroup {
+  hipEvent_t ev = nullptr;
+  bool pending = false;    // ev recorded and not yet waited for
+  bool unguarded = false;  // no single event covers the group's calls
+  hipStream_t stream = nullptr;
+};
 struct Ring {
   StagingSlot slot[kSlots];
+  SlotGroup grp[kSlots / kGroup];
   int next = 0;
 };
 std::mutex g_mu;  // guards the rings, the epoch map and the timing state
@@ -36,22 +47,40 @@ std::map<int, Ring> g_rings;                 // per device
 std::map<const void*, uint32_t> g_ws_tag;  // last tag a fused call used, per workspace
 thread_local PlanScratch t_scratch;
 
-int acquire_slot(size_t n, StagingSlot** out) {
+struct SlotRef {
+  Ring* ring = nullptr;
+  int index = 0;
+  void* host() const { return ring->slot[index].host; }
+};
+
+int acquire_slot(size_t n, hipStream_t stream, SlotRef* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   Ring& ring = g_rings[dev];
-  StagingSlot& s = ring.slot[ring.next];
-  ring.next = (ring.next + 1) % kSlots;
-  if (s.pending) {
-    e = hipEventSynchronize(s.ev);
-    if (e != hipSuccess) return hip_fail(e, "staging: hipEventSynchronize");
-    s.pending = false;
+  const int i = ring.next;
+  SlotGroup& grp = ring.grp[i / kGroup];
+  if (i % kGroup == 0) {  // the group comes round again: its previous calls must be done
+    if (grp.pending) {
+      e = hipEventSynchronize(grp.ev);
+      if (e != hipSuccess) return hip_fail(e, "staging: hipEventSynchronize");
+      grp.pending = false;
+    }
+    if (grp.unguarded) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "staging: hipDeviceSynchronize");
+      grp.unguarded = false;
+    }
+    if (!grp.ev) {
+      e = hipEventCreateWithFlags(&grp.ev, hipEventDisableTiming);
+      if (e != hipSuccess) { grp.ev = nullptr; return hip_fail(e, "staging: hipEventCreate"); }
+    }
+    grp.stream = stream;
+  } else if (stream != grp.stream) {
+    grp.unguarded = true;
   }
-  if (!s.ev) {
-    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
-    if (e != hipSuccess) { s.ev = nullptr; return hip_fail(e, "staging: hipEventCreate"); }
-  }
+  ring.next = (i + 1) % kSlots;
+  StagingSlot& s = ring.slot[i];
   if (s.cap < n) {
     if (s.host) (void)hipHostFree(s.host);
     s.host = nullptr;
@@ -59,10 +88,34 @@ int acquire_slot(size_t n, StagingSlot** out) {
     size_t cap = 1 << 16;
     while (cap < n) cap <<= 1;
     e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
-    if (e != hipSuccess) { s.host = nullptr; return hip_fail(e, "staging: hipHostMalloc"); }
+    if (e != hipSuccess) {
+      s.host = nullptr;
+      grp.unguarded = true;
+      return hip_fail(e, "staging: hipHostMalloc");
+    }
     s.cap = cap;
   }
-  *out = &s;
+  out->ring = &ring;
+  out->index = i;
+  return SLORA_OK;
+}
+
+// After a call's launches (ok) or a failure after acquire_slot (!ok): the group's last
+// call records the group's event.
+int release_slot(const SlotRef& r, hipStream_t stream, bool ok) {
+  SlotGroup& grp = r.ring->grp[r.index / kGroup];
+  if (!ok) {
+    grp.unguarded = true;
+    return SLORA_OK;
+  }
+  if (r.index % kGroup == kGroup - 1 && !grp.unguarded) {
+    const hipError_t e = hipEventRecord(grp.ev, stream);
+    if (e != hipSuccess) {
+      grp.unguarded = true;
+      return hip_fail(e, "staging: hipEventRecord");
+    }
+    grp.pending = true;
+  }
   return SLORA_OK;
 }
 
@@ -105,6 +158,10 @@ enum Mode { kShrink = 1, kExpand = 2, kApply = 3 };
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
+int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv, const void* x,
+                float* v_out, const float* v_in, void* y, void* ws, int64_t ws_bytes,
+                const WsLayout& lay, hipStream_t s, int mode);
+
 int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out,
         const float* v_in, void* y, void* ws, int64_t ws_bytes, void* stream, int mode) {
   clear_error();
@@ -127,12 +184,20 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
   if (pv.n_routed == 0) return SLORA_OK;
 
   std::lock_guard<std::mutex> lk(g_mu);
-  StagingSlot* slot = nullptr;
-  int rc = acquire_slot((size_t)bytes, &slot);
-  if (rc) return rc;
-  plan_write(L, R, &t_scratch, slot->host, &pv);  // kernels read this host buffer directly
-
   hipStream_t s = (hipStream_t)stream;
+  SlotRef slot;
+  int rc = acquire_slot((size_t)bytes, s, &slot);
+  if (rc) return rc;
+  plan_write(L, R, &t_scratch, slot.host(), &pv);  // kernels read this host buffer directly
+  rc = launch_plan(L, R, pv, x, v_out, v_in, y, ws, ws_bytes, lay, s, mode);
+  const int rc2 = release_slot(slot, s, rc == SLORA_OK);
+  return rc ? rc : rc2;
+}
+
+// The launches of one planned call (the work list is in a pinned staging slot).
+int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv, const void* x,
+                float* v_out, const float* v_in, void* y, void* ws, int64_t ws_bytes,
+                const WsLayout& lay, hipStream_t s, int mode) {
   uint8_t* wsb = (uint8_t*)ws;
   Geom g;
   g.pool = (const uint16_t*)L->pool;
@@ -209,9 +274,6 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
     }
     if (e != hipSuccess) return hip_fail(e, "mbgmv launch");
   }
-  e = hipEventRecord(slot->ev, s);
-  if (e != hipSuccess) return hip_fail(e, "staging: hipEventRecord");
-  slot->pending = true;
   return SLORA_OK;
 }
 

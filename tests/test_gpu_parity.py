@@ -290,6 +290,42 @@ def test_fetch_waits_and_free_state(rt):
     inst.close()
 
 
+@pytest.mark.parametrize("n_streams", [1, 2], ids=["one-stream", "two-streams"])
+def test_staging_ring_reuse(rt, n_streams):
+    """Work lists sit in a ring of pinned slots that the host refills once the kernels
+    that read them are done. With the streams held back by a bounded spin, the host runs
+    more than two laps of the ring ahead of the GPU; every call must still run its own
+    plan (three workloads alternate, so a slot refilled too early holds another plan)."""
+    say(f"[gpu] staging ring reuse, {n_streams} stream(s)")
+    wls = [workloads.random_small(seed=110 + i, n_tokens=30 + 9 * i, n_segments=i) for i in range(3)]
+    insts = [rt.PagedLoRA(wl) for wl in wls]
+    refs = [oracle_ref(wl, 0)[0] for wl in wls]
+    ins = [inst.inputs(0) for inst in insts]
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(20_000_000)  # bounded spin: the GPU falls behind the host
+    outs = []
+    for i in range(40):
+        k, s = i % 3, streams[i % n_streams]
+        call = insts[k].call(0)
+        x, y0 = ins[k]
+        with torch.cuda.stream(s):
+            y = y0.clone()
+            ws = insts[k].workspace(call)
+            insts[k].apply(call, x, y, ws, stream=s)
+        outs.append((k, y, ws))
+    torch.cuda.synchronize()
+    first = {}
+    for i, (k, y, ws) in enumerate(outs):
+        bits = y.cpu().numpy().view(np.uint16)
+        check_close(bits, refs[k], wls[k].dtype, f"call {i} (workload {k})")
+        assert np.array_equal(bits, first.setdefault(k, bits)), f"call {i} differs from workload {k}'s first call"
+    for inst in insts:
+        inst.close()
+
+
 LARGE = [("mixed_13b", 1), ("mlp_asym", 1), ("prefill_sgmv", 0), ("mixed_13b", 0),
          ("mlp_asym", 2), ("mlp_asym", 0)]
 
