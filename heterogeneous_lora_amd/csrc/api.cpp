@@ -239,17 +239,38 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
       v_stride = L->r_max;
     }
     const int64_t stride = (int64_t)R->n_tokens * v_stride;
+    // Tiles come in descending rank. Ranks above 64 need the widest kernels, which keep
+    // fewer waves per SIMD. With enough tiles of both kinds, each kind gets its own
+    // launch, timed as one interval (the first launch records the start, the second
+    // the stop); with few tiles on one side the second launch costs more than the
+    // narrower kernels save.
+    int32_t hi = 0;
+    while (hi < pv.n_sg && pv.sg[hi].rank > 64) ++hi;
+    const bool split = hi >= kSgSplitTiles && pv.n_sg - hi >= kSgSplitTiles;
+    auto by_rank = [&](const LaunchEvents& le, auto&& one) -> hipError_t {
+      if (!split) return one(0, pv.n_sg, pv.sg_max_rank, le);
+      LaunchEvents first = le, second = le;
+      first.stop = nullptr;
+      second.start = nullptr;
+      const hipError_t e1 = one(0, hi, pv.sg_max_rank, first);
+      if (e1 != hipSuccess) return e1;
+      return one(hi, pv.n_sg - hi, pv.sg[hi].rank, second);
+    };
     if (mode & kShrink) {
       e = timed_launch(SLORA_K_SGMV_SHRINK, s, [&](const LaunchEvents& le) {
-        return launch_sgmv_shrink(g, pv.tok, pv.sg, pv.n_sg, pv.sg_max_rank, sp.ksplit, sp.kc, x,
-                                  vpart, v_stride, stride, s, le);
+        return by_rank(le, [&](int32_t t0, int32_t nt, int32_t mr, const LaunchEvents& l) {
+          return launch_sgmv_shrink(g, pv.tok, pv.sg + t0, nt, mr, sp.ksplit, sp.kc, x, vpart,
+                                    v_stride, stride, s, l);
+        });
       });
       if (e != hipSuccess) return hip_fail(e, "sgmv_shrink launch");
     }
     if (mode & kExpand) {
       e = timed_launch(SLORA_K_SGMV_EXPAND, s, [&](const LaunchEvents& le) {
-        return launch_sgmv_expand(g, pv.tok, pv.sg, pv.n_sg, pv.sg_max_rank, sp.ksplit, vpart,
-                                  v_stride, stride, y, s, le);
+        return by_rank(le, [&](int32_t t0, int32_t nt, int32_t mr, const LaunchEvents& l) {
+          return launch_sgmv_expand(g, pv.tok, pv.sg + t0, nt, mr, sp.ksplit, vpart, v_stride,
+                                    stride, y, s, l);
+        });
       });
       if (e != hipSuccess) return hip_fail(e, "sgmv_expand launch");
     }

@@ -24,6 +24,7 @@ constexpr int kMbExpandTok = 2;     // MBGMV expand: tokens per workgroup
 constexpr int kMbWaveCols = 512;    // MBGMV expand: output columns per wave (64 lanes x 8)
 constexpr int kMbRowsPerWave = 16;  // MBGMV expand: B rows a wave keeps in flight
 constexpr int kSgTile = 64;         // SGMV: tokens per tile
+constexpr int kSgSplitTiles = 64;    // SGMV: tiles of ranks <= 64 and > 64, each, for separate launches
 constexpr int kAutoSgmvTok = 4;     // AUTO: an adapter's per-token ids go to SGMV from this many
 constexpr int kAutoSgmvBatch = 256; // AUTO: ... when at least this many such tokens (or segments run)
 constexpr int kXcds = 8;            // XCDs (dies, each with its own L2) workgroups are dealt to in turn
