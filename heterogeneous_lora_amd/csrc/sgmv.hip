@@ -206,7 +206,8 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KB)) void sgmv_expand_ker
   constexpr int kRp = KB * kStep;     // padded rank
   constexpr int kVPitch = kRp + 8;    // v row pitch in elements
   __shared__ uint16_t vs[kTileRows * kVPitch];
-  __shared__ uint16_t bs[KB * kChunkRows * kBPitch];
+  constexpr int kBBufs = KB <= 2 ? 2 : 1;  // two B stages: one barrier per pass
+  __shared__ uint16_t bs[kBBufs * KB * kChunkRows * kBPitch];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
   const SgTile tl = tiles[blockIdx.x];
@@ -254,12 +255,12 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KB)) void sgmv_expand_ker
         b[ch][i] = ld16(p);
       }
   };
-  auto store_b = [&](const uint4 (&b)[KB][kBLoads]) {
+  auto store_b = [&](const uint4 (&b)[KB][kBLoads], int buf) {
 #pragma unroll
     for (int ch = 0; ch < KB; ++ch)
 #pragma unroll
       for (int i = 0; i < kBLoads; ++i) {
-        uint2* d = reinterpret_cast<uint2*>(&bs[(ch * kChunkRows + row0 + i * kRowStep) * kBPitch + slot * 8]);
+        uint2* d = reinterpret_cast<uint2*>(&bs[((buf * KB + ch) * kChunkRows + row0 + i * kRowStep) * kBPitch + slot * 8]);
         d[0] = make_uint2(b[ch][i].x, b[ch][i].y);
         d[1] = make_uint2(b[ch][i].z, b[ch][i].w);
       }
@@ -322,13 +323,17 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KB)) void sgmv_expand_ker
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[h][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();  // v is staged / the previous pass's rows have been read
-    store_b(bn);
+    // With two stages, the one this pass writes was last read in pass - 2, and every wave
+    // had finished those reads before it passed pass - 1's barrier; one stage needs a
+    // barrier here. Pass 0 waits for v to be staged.
+    const int buf = kBBufs == 2 ? (pass & 1) : 0;
+    if (kBBufs == 1 || pass == 0) __syncthreads();
+    store_b(bn, buf);
     if (pass + 1 < n_pass) load_b(bn, pass + 1);
     __syncthreads();
 #pragma unroll
     for (int ch = 0; ch < KB; ++ch) {
-      const uint16_t* bsc = bs + ch * kChunkRows * kBPitch;
+      const uint16_t* bsc = bs + (buf * KB + ch) * kChunkRows * kBPitch;
       // v^T operand: token tb * 16 + li, k = ch * 32 + kg * 8 + [0, 8)
       uint4 vo[4];
 #pragma unroll
