@@ -326,6 +326,39 @@ def test_staging_ring_reuse(rt, n_streams):
         inst.close()
 
 
+def _rank_split_case():
+    """160 short segments over two adapters of rank above 64 and two below, plus
+    per-token ids: enough tiles of each kind that SGMV runs them as two launches."""
+    import dataclasses
+    wl = workloads.random_small(130, dtype="bf16", n_adapters=4, d_in=264, d_out=520,
+                                page_elems=256, rank_choices=(8,))
+    ranks = np.array([128, 16, 72, 40], np.int32)
+    lens = 1 + (np.arange(160) * 7) % 5
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    seg_ad = (np.arange(160) % 4).astype(np.int32)
+    tok = ((np.arange(40) * 3) % 5 - 1).astype(np.int32)
+    pages = int(ranks.sum()) * (-(-264 // 256) + -(-520 // 256)) + 17
+    return dataclasses.replace(wl, ranks=ranks, scales=workloads._scales(ranks), seg_offsets=offs,
+                               seg_adapter=seg_ad, token_adapter=tok, n_pages=pages)
+
+
+@pytest.mark.parametrize("policy", [0, 2], ids=["auto", "sgmv"])
+def test_rank_split_launches(rt, policy):
+    """SGMV tiles of ranks above 64 and the rest in separate launches (82 tiles each):
+    every output row against the oracle."""
+    from heterogeneous_lora_amd import _lib
+    wl = _rank_split_case()
+    say(f"[gpu] rank-split SGMV launches, policy={policy}")
+    inst = rt.PagedLoRA(wl)
+    groups, _ = _lib.plan_inspect(inst.call(0, policy))
+    sg = groups[groups[:, 0] == 1]
+    assert (sg[:, 4] > 64).sum() >= 64 and (sg[:, 4] <= 64).sum() >= 64
+    y, inst = _run(rt, wl, policy=policy, inst=inst)
+    ref, _ = oracle_ref(wl, 0)
+    check_close(y, ref, wl.dtype, "rank split")
+    inst.close()
+
+
 LARGE = [("mixed_13b", 1), ("mlp_asym", 1), ("prefill_sgmv", 0), ("mixed_13b", 0),
          ("mlp_asym", 2), ("mlp_asym", 0)]
 
