@@ -7,7 +7,7 @@
 // One kernel runs both halves of the LoRA product so that a decode batch is a
 // single launch (a decode batch moves tens of MB; two launches would each pay the
 // fixed launch and ramp cost, which is of the order of the whole transfer). The
-// work list (64-byte items, token ids inline) is read from pinned host memory.
+// work list (32-byte items, token ids inline) is read from pinned host memory.
 //
 //   shrink items (first in the grid): (group of <= 4 tokens, 8 rows of A^T),
 //     4 waves x 2 rows. The group's x goes straight from global memory into LDS
