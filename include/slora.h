@@ -20,8 +20,12 @@
  *
  * Memory model. Every device buffer (pool, page table, x, y, v, workspace) is
  * allocated and owned by the caller. The library owns host bookkeeping (the pool
- * handle) and a small pinned staging ring for work lists. All compute calls are
- * asynchronous on the stream they are given; argument validation is synchronous.
+ * handle) and a small pinned staging ring for work lists (16 slots, reused in
+ * groups of 8 calls). All compute calls are asynchronous on the stream they are
+ * given; argument validation is synchronous. A call blocks the host only when it
+ * reaches a group of slots whose previous calls (8 to 16 calls back) have not
+ * finished on the GPU; if that group's calls used more than one stream, the wait is
+ * a device synchronization.
  *
  * Paged layout. The pool is n_pages pages of page_elems elements of one dtype.
  * A page holds one chunk of one row: adapter i's projection p occupies, for each
