@@ -39,36 +39,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(wl, proj, policy):
-    """Per-kernel algorithmic bytes and flops of one apply of projection `proj`.
+def algorithmic(wl, proj, call):
+    """Per-kernel algorithmic bytes and flops of one apply of projection `proj`, split by
+    the family the library's own plan (slora_plan_inspect) gives each group of tokens.
 
-    Weights of every distinct active adapter are read once; x is read once, y0 read
-    and y written once. Intermediates (v), page tails and work lists are not counted.
-    Tokens routed by segment go to SGMV under the default policy, per-token ids to
-    MBGMV; the policies override that split."""
+    Weights of every distinct adapter a family uses are read once by that family's
+    kernels; x is read once, y0 read and y written once per routed token. Intermediates
+    (v), page tails and work lists are not counted."""
+    from heterogeneous_lora_amd import _lib
     p = wl.projections[proj]
     e = 2
-    seg_ids = np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets))
-    fam = {"mbgmv": [], "sgmv": []}
-    for a in seg_ids:
-        fam["mbgmv" if policy == 1 else "sgmv"].append(int(a))
-    for a in wl.token_adapter:
-        fam["sgmv" if policy == 2 else "mbgmv"].append(int(a))
+    groups, _ = _lib.plan_inspect(call)
     out = {}
-    for f, ids in fam.items():
-        ids = np.array([a for a in ids if a >= 0 and wl.ranks[a] > 0], np.int64)
-        T = ids.size
-        uniq = np.unique(ids)
-        r = wl.ranks[uniq].astype(np.int64)
-        out[f + "_shrink"] = dict(bytes=int(r.sum() * p.d_in * e + T * p.d_in * e),
-                                  flops=int(2 * wl.ranks[ids].astype(np.int64).sum() * p.d_in),
-                                  tokens=int(T), adapters=int(uniq.size))
-        out[f + "_expand"] = dict(bytes=int(r.sum() * p.d_out * e + 2 * T * p.d_out * e),
-                                  flops=int(2 * wl.ranks[ids].astype(np.int64).sum() * p.d_out),
-                                  tokens=int(T), adapters=int(uniq.size))
-        out[f + "_fused"] = {k: out[f + "_shrink"][k] + out[f + "_expand"][k]
-                             for k in ("bytes", "flops")}
-        out[f + "_fused"].update(tokens=int(T), adapters=int(uniq.size))
+    for fam_id, f in ((0, "mbgmv"), (1, "sgmv")):
+        g = groups[groups[:, 0] == fam_id] if len(groups) else np.zeros((0, 5), np.int32)
+        T = int(g[:, 2].sum())
+        rank_of = {int(row[3]): int(row[4]) for row in g}  # adapters by first page-table entry
+        r_sum = sum(rank_of.values())
+        tok_r = int((g[:, 2].astype(np.int64) * g[:, 4].astype(np.int64)).sum())
+        out[f + "_shrink"] = dict(bytes=int(r_sum * p.d_in * e + T * p.d_in * e),
+                                  flops=int(2 * tok_r * p.d_in), tokens=T, adapters=len(rank_of))
+        out[f + "_expand"] = dict(bytes=int(r_sum * p.d_out * e + 2 * T * p.d_out * e),
+                                  flops=int(2 * tok_r * p.d_out), tokens=T, adapters=len(rank_of))
+        out[f + "_fused"] = {k: out[f + "_shrink"][k] + out[f + "_expand"][k] for k in ("bytes", "flops")}
+        out[f + "_fused"].update(tokens=T, adapters=len(rank_of))
     return out
 
 
@@ -289,7 +283,7 @@ def main():
         f"{value:.4g} tokens/s")
 
     # per-kernel roofline (bytes and flops averaged over the projections' launches)
-    alg = [algorithmic(wl, p, policy) for p in range(n_proj)]
+    alg = [algorithmic(wl, p, insts[0][1][p]) for p in range(n_proj)]
     kernels = {}
     for k, (n, ms) in timing.items():
         if n == 0:

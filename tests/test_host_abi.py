@@ -9,6 +9,7 @@
 """
 
 import re
+import sys
 import os
 
 import numpy as np
@@ -267,3 +268,26 @@ def test_plan_matches_model(wl_name, policy):
     routed = np.nonzero((ids >= 0) & (wl.ranks[np.maximum(ids, 0)] > 0))[0]
     assert np.array_equal(np.sort(toks), routed)
     pool.destroy()
+
+
+def test_bench_accounting_follows_the_plan():
+    """bench.py splits algorithmic bytes between the families by the library's own plan:
+    every routed token is counted once, and a pure decode batch counts each active
+    adapter's weights once plus x, y0 and y per token."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    for name in ("decode_7b", "mlp_asym"):
+        wl = workloads.make(name)
+        call, pool, pt, base = _call(wl)
+        a = bench.algorithmic(wl, 0, call)
+        ids = np.concatenate([np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets)), wl.token_adapter])
+        routed = ids[(ids >= 0) & (wl.ranks[np.maximum(ids, 0)] > 0)]
+        assert a["mbgmv_fused"]["tokens"] + a["sgmv_fused"]["tokens"] == routed.size
+        if name == "decode_7b":
+            p = wl.projections[0]
+            w = sum(int(wl.ranks[x]) for x in np.unique(routed)) * (p.d_in + p.d_out) * 2
+            assert a["mbgmv_fused"]["bytes"] == w + routed.size * (p.d_in + 2 * p.d_out) * 2
+            assert a["sgmv_fused"]["tokens"] == 0
+        else:  # AUTO sends the adapters with several tokens to SGMV tiles
+            assert a["sgmv_fused"]["tokens"] > a["mbgmv_fused"]["tokens"] > 0
+        pool.destroy()
