@@ -73,6 +73,64 @@ def test_small_parity(rt, kw, policy):
     inst.close()
 
 
+EDGE = [
+    # one decode token, one adapter
+    dict(seed=301, n_tokens=1, n_segments=0, p_none=0.0, rank_choices=(16,), n_adapters=1,
+         d_in=256, d_out=256, page_elems=256),
+    # one prefill token in a segment of its own, then one decode token
+    dict(seed=326, n_tokens=2, n_segments=1, p_none=0.0, rank_choices=(8,), n_adapters=2,
+         d_in=512, d_out=264, page_elems=128),
+    # A^T rows at the 32-page limit, B rows over 33 pages with a ragged last page, rank 128
+    dict(seed=303, d_in=2048, d_out=2056, page_elems=64, n_tokens=40, n_segments=2,
+         rank_choices=(1, 128), n_adapters=3, p_none=0.0),
+]
+
+
+@pytest.mark.parametrize("kw", EDGE, ids=[f"e{k['seed']}" for k in EDGE])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
+def test_edge_parity(rt, kw, policy):
+    wl = workloads.random_small(**kw)
+    routed = np.concatenate([np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets)), wl.token_adapter])
+    assert (routed >= 0).any()
+    say(f"[gpu] edge parity {kw} policy={policy}")
+    y, inst = _run(rt, wl, policy=policy)
+    ref, _ = oracle_ref(wl, 0)
+    check_close(y, ref, wl.dtype, f"edge {kw}")
+    inst.close()
+
+
+def test_empty_and_idle_calls(rt):
+    """A call with no tokens and a call whose tokens all have no adapter (id -1 or rank
+    0) succeed and leave y exactly as it was."""
+    from heterogeneous_lora_amd import _lib
+    wl = workloads.random_small(306, n_tokens=24, n_segments=2, rank_choices=(0, 8), n_adapters=3)
+    say("[gpu] empty and idle calls")
+    inst = rt.PagedLoRA(wl)
+    x, y = inst.inputs(0)
+    y_before = y.clone()
+    stream = torch.cuda.current_stream().cuda_stream
+    zero_rank = [a for a in range(wl.n_adapters) if wl.ranks[a] == 0]
+    idle = lambda ids: np.where(np.arange(ids.size) % 2 == 0, -1,
+                                zero_rank[0] if zero_rank else -1).astype(np.int32)
+    for name, over in (("empty", dict(n_tokens=0, seg_offsets=np.zeros(1, np.int32),
+                                      seg_adapter=np.zeros(0, np.int32),
+                                      token_adapter=np.zeros(0, np.int32))),
+                       ("idle", dict(seg_adapter=idle(wl.seg_adapter),
+                                     token_adapter=idle(wl.token_adapter)))):
+        c = _lib.Call(pool_ptr=inst.pool_t.data_ptr(), n_pages=wl.n_pages, page_elems=wl.page_elems,
+                      dtype=wl.dtype, d_in=wl.projections[0].d_in, d_out=wl.projections[0].d_out,
+                      page_table_ptr=inst.pt_dev[0].data_ptr(), page_table_len=inst.pt_len[0],
+                      base=inst.base[0], rank=wl.ranks, scale=wl.scales.astype(np.float32),
+                      r_max=inst.r_max, policy=0,
+                      **{**dict(n_tokens=wl.n_tokens, seg_offsets=wl.seg_offsets,
+                                seg_adapter=wl.seg_adapter, token_adapter=wl.token_adapter), **over})
+        ws = inst.workspace(c)
+        _lib.apply(c, x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_before), name
+    inst.close()
+
+
 @pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 def test_tiny_decode_parity(rt, policy):
     wl = workloads.tiny(0)

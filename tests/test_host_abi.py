@@ -163,6 +163,13 @@ def test_validation_rejects_bad_calls():
         "page_table_short": (dict(page_table_len=int(pt.size) - 1), _lib.E_INVALID),
         "d_in_not_multiple_of_8": (dict(d_in=wl.projections[0].d_in + 4), _lib.E_INVALID),
         "bad_policy": (dict(policy=7), _lib.E_INVALID),
+        # a row may span at most 32 pages (a wave holds the page ids of two A^T rows)
+        "d_in_spans_33_pages": (dict(d_in=33 * wl.page_elems), _lib.E_INVALID),
+        "scale_not_finite": (dict(scale=np.full(wl.n_adapters, np.nan, np.float32)), _lib.E_INVALID),
+        "empty_segment_bad_id": (dict(seg_offsets=np.array([0, 0, 5, 9], np.int32),
+                                      seg_adapter=np.array([wl.n_adapters, 0, 1], np.int32),
+                                      token_adapter=np.zeros(wl.n_tokens - 9, np.int32)),
+                                 _lib.E_INVALID),
     }
     assert len(wl.token_adapter) > 0 and used
     for name, (over, code) in cases.items():
@@ -175,6 +182,10 @@ def test_validation_rejects_bad_calls():
     # an all-idle batch (every id -1) does nothing and succeeds without touching HIP
     c, _, _, _ = _call(wl, pool=pool, seg_adapter=np.full_like(wl.seg_adapter, -1),
                        token_adapter=np.full_like(wl.token_adapter, -1))
+    assert _apply_code(c) == 0
+    # so does an empty call (no tokens, no segments)
+    c, _, _, _ = _call(wl, pool=pool, n_tokens=0, seg_offsets=np.zeros(1, np.int32),
+                       seg_adapter=np.zeros(0, np.int32), token_adapter=np.zeros(0, np.int32))
     assert _apply_code(c) == 0
     pool.destroy()
 
