@@ -14,9 +14,9 @@
 //     page table) are both contiguous in j, so both operands are plain 16-byte
 //     loads. Each wave owns 16 tokens and reads its x rows straight from global
 //     memory; the A^T rows, which all 4 waves need, pass through LDS once per
-//     workgroup. The k-ranges give the launch enough workgroups to fill the chip;
-//     the expand adds the ranges' partial sums in range order, so the result does
-//     not depend on scheduling.
+//     workgroup. The k-ranges give the launch enough workgroups to fill the chip
+//     without spilling into a second round; the expand adds the ranges' partial
+//     sums in range order, so the result does not depend on scheduling.
 //   expand (tile, 1024 output columns): y[t, n] = RNE(y0 + s * sum_k v[t, k] B[k, n]).
 //     The product is computed transposed, D = B^T v^T, so that each lane ends up
 //     with 8 consecutive output columns of one token (16-byte y0 loads and y
@@ -77,6 +77,8 @@ constexpr int kSegs = kBatch / 8;  // 16-byte segments per slab row
 // keep more loads in flight.
 constexpr int shrink_waves(int nb) { return nb <= 4 ? 4 : 1; }
 constexpr int expand_waves(int kb) { return kb <= 1 ? 4 : kb <= 2 ? 3 : 1; }
+static_assert(kSgShrinkPerCu == shrink_waves(4), "shrink workgroups per CU (4 waves each)");
+constexpr int32_t kSgMinSplit = 3;
 
 template <int DT, int NB>
 __global__ __launch_bounds__(64 * kWaves, shrink_waves(NB)) void sgmv_shrink_kernel(
@@ -415,9 +417,14 @@ hipError_t expand_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int
 
 }  // namespace
 
-SgSplit sg_split(int32_t d_in, int32_t n_tiles) {
+SgSplit sg_split(int32_t d_in, int32_t n_tiles, int32_t slots) {
   SgSplit o;
-  int32_t ks = n_tiles > 0 ? (1024 + n_tiles - 1) / n_tiles : 1;
+  // k-ranges: a workgroup walks its range as a chain of dependent batches, and the
+  // expand reads every range's partial sums. Three ranges measured best on both the
+  // prefill batch (290 tiles) and the MLP batch (~480 tiles); more are used only while
+  // every (tile, k-range) workgroup still fits on the device at once, since a launch
+  // that spills a little into a second round ends with a tail of lone chains.
+  int32_t ks = n_tiles > 0 ? std::max(kSgMinSplit, slots / n_tiles) : 1;
   ks = std::max(1, std::min(ks, sg_max_split(d_in)));
   const int32_t per = (d_in + ks - 1) / ks;
   o.kc = (per + kRound - 1) / kRound * kRound;
