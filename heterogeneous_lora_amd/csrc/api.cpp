@@ -156,20 +156,6 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
 
 enum Mode { kShrink = 1, kExpand = 2, kApply = 3 };
 
-// Compute units of the current device (cached per device; callers hold g_mu).
-int compute_units() {
-  static std::map<int, int> cus;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  auto f = cus.find(dev);
-  if (f != cus.end()) return f->second;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-    (void)hipGetLastError();
-    n = 256;
-  }
-  return cus[dev] = n;
-}
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -245,7 +231,7 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
     // apply: k-range partials in the workspace; shrink / expand only: one range,
     // straight into / out of the caller's v
     int32_t v_stride = sg_v_stride(L->r_max);
-    SgSplit sp = sg_split(L->d_in, pv.n_sg, kSgShrinkPerCu * compute_units());
+    SgSplit sp = sg_split(L->d_in, pv.n_sg, sgmv_shrink_resident(pv.sg_max_rank, L->dtype));
     float* vpart = (float*)(wsb + lay.sg_off);
     if (mode != kApply) {
       sp.ksplit = 1;

@@ -26,6 +26,10 @@
 //     operand read out column-wise, while the next pass's y0 is already loading.
 #include <algorithm>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "device_common.h"
 
 namespace slora {
@@ -77,8 +81,9 @@ constexpr int kSegs = kBatch / 8;  // 16-byte segments per slab row
 // keep more loads in flight.
 constexpr int shrink_waves(int nb) { return nb <= 4 ? 4 : 1; }
 constexpr int expand_waves(int kb) { return kb <= 1 ? 4 : kb <= 2 ? 3 : 1; }
-static_assert(kSgShrinkPerCu == shrink_waves(4), "shrink workgroups per CU (4 waves each)");
 constexpr int32_t kSgMinSplit = 3;
+// 16-row blocks of rank rows the shrink template for ranks up to max_rank holds.
+constexpr int shrink_nb(int max_rank) { return max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8; }
 
 template <int DT, int NB>
 __global__ __launch_bounds__(64 * kWaves, shrink_waves(NB)) void sgmv_shrink_kernel(
@@ -417,13 +422,40 @@ hipError_t expand_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int
 
 }  // namespace
 
+int sgmv_shrink_resident(int32_t max_rank, int32_t dtype) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int>, int> cache;
+  const int nb = shrink_nb(max_rank);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_tuple(dev, nb, (int)dtype);
+  auto f = cache.find(key);
+  if (f != cache.end()) return f->second;
+  const void* k = nullptr;
+  if (dtype == SLORA_F16)
+    k = nb == 1 ? (const void*)sgmv_shrink_kernel<SLORA_F16, 1> : nb == 2 ? (const void*)sgmv_shrink_kernel<SLORA_F16, 2>
+      : nb == 4 ? (const void*)sgmv_shrink_kernel<SLORA_F16, 4> : (const void*)sgmv_shrink_kernel<SLORA_F16, 8>;
+  else
+    k = nb == 1 ? (const void*)sgmv_shrink_kernel<SLORA_BF16, 1> : nb == 2 ? (const void*)sgmv_shrink_kernel<SLORA_BF16, 2>
+      : nb == 4 ? (const void*)sgmv_shrink_kernel<SLORA_BF16, 4> : (const void*)sgmv_shrink_kernel<SLORA_BF16, 8>;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * kWaves, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return cache[key] = per_cu * cus;
+}
+
 SgSplit sg_split(int32_t d_in, int32_t n_tiles, int32_t slots) {
   SgSplit o;
   // k-ranges: a workgroup walks its range as a chain of dependent batches, and the
-  // expand reads every range's partial sums. Three ranges measured best on both the
-  // prefill batch (290 tiles) and the MLP batch (~480 tiles); more are used only while
-  // every (tile, k-range) workgroup still fits on the device at once, since a launch
-  // that spills a little into a second round ends with a tail of lone chains.
+  // expand reads every range's partial sums. Three ranges measured best on the
+  // prefill batch (290 tiles), the MLP batch (~480 tiles) and the mixed batch (~130
+  // tiles, ranks to 128); more are used only while every (tile, k-range) workgroup
+  // still fits on the device at once, since a launch that spills a little into a
+  // second round ends with a tail of lone chains.
   int32_t ks = n_tiles > 0 ? std::max(kSgMinSplit, slots / n_tiles) : 1;
   ks = std::max(1, std::min(ks, sg_max_split(d_in)));
   const int32_t per = (d_in + ks - 1) / ks;
@@ -439,7 +471,7 @@ hipError_t launch_sgmv_shrink(const Geom& g, const int32_t* tok, const SgTile* t
   if (n_tiles <= 0) return hipSuccess;
   if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit || kc % kRound)
     return hipErrorInvalidValue;
-  const int nb = max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8;
+  const int nb = shrink_nb(max_rank);
   return g.dtype == SLORA_F16
              ? shrink_dt<SLORA_F16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, v_stride, split_stride, s, ev)
              : shrink_dt<SLORA_BF16>(g, tok, tiles, n_tiles, ksplit, kc, nb, x, vpart, v_stride, split_stride, s, ev);
