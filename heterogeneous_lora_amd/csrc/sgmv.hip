@@ -78,9 +78,12 @@ constexpr int kSegs = kBatch / 8;  // 16-byte segments per slab row
 // compiler spreads these kernels over the unified register file (accumulation
 // registers included) and lands at 3 (shrink, NB = 4) or 2 (expand, KB = 2) waves per
 // SIMD; the same code fits 4 and 3 without spilling, and the extra resident waves
-// keep more loads in flight.
+// keep more loads in flight. The widest expand (KB = 4, ranks above 64) spills ~16
+// registers per lane at 3 waves per SIMD and is still faster than at 2 (a launch over
+// all of a mixed batch's tiles: 73 -> 63 us). The widest shrink is held to 2 by its
+// 64 KB LDS slab whatever its registers.
 constexpr int shrink_waves(int nb) { return nb <= 4 ? 4 : 1; }
-constexpr int expand_waves(int kb) { return kb <= 1 ? 4 : kb <= 2 ? 3 : 1; }
+constexpr int expand_waves(int kb) { return kb <= 1 ? 4 : 3; }
 constexpr int32_t kSgMinSplit = 3;
 // 16-row blocks of rank rows the shrink template for ranks up to max_rank holds.
 constexpr int shrink_nb(int max_rank) { return max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8; }
