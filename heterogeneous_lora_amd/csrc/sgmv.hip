@@ -381,14 +381,22 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KB)) void sgmv_expand_ker
   };
 
   // y0 of the next pass loads while a pass multiplies (two named buffers)
-  uint4 ya[4], yb[4];
-  load_y0(ya, 0);
-  for (int pass = 0; pass < n_pass; pass += 2) {
-    if (pass + 1 < n_pass) load_y0(yb, pass + 1);
-    run_pass(pass, ya);
-    if (pass + 1 >= n_pass) break;
-    if (pass + 2 < n_pass) load_y0(ya, pass + 2);
-    run_pass(pass + 1, yb);
+  if constexpr (KB >= 4) {  // one y0 buffer, loaded as its pass begins
+    uint4 ya[4];
+    for (int pass = 0; pass < n_pass; ++pass) {
+      load_y0(ya, pass);
+      run_pass(pass, ya);
+    }
+  } else {
+    uint4 ya[4], yb[4];
+    load_y0(ya, 0);
+    for (int pass = 0; pass < n_pass; pass += 2) {
+      if (pass + 1 < n_pass) load_y0(yb, pass + 1);
+      run_pass(pass, ya);
+      if (pass + 1 >= n_pass) break;
+      if (pass + 2 < n_pass) load_y0(ya, pass + 2);
+      run_pass(pass + 1, yb);
+    }
   }
 }
 
