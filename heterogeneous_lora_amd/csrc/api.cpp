@@ -156,7 +156,6 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
 
 enum Mode { kShrink = 1, kExpand = 2, kApply = 3 };
 
-
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv, const void* x,

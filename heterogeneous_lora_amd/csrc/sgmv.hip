@@ -380,8 +380,10 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KB)) void sgmv_expand_ker
     }
   };
 
-  // y0 of the next pass loads while a pass multiplies (two named buffers)
-  if constexpr (KB >= 4) {  // one y0 buffer, loaded as its pass begins
+  // y0 of the next pass loads while a pass multiplies (two named buffers), except in
+  // the widest template, which is short of registers: there one y0 buffer is loaded as
+  // its pass begins and arrives while the pass stages B and multiplies
+  if constexpr (KB >= 4) {
     uint4 ya[4];
     for (int pass = 0; pass < n_pass; ++pass) {
       load_y0(ya, pass);
