@@ -55,6 +55,12 @@ SMALL = [
          rank_choices=(5, 16, 33), n_adapters=6),
     dict(seed=106, dtype="bf16", d_in=2048, d_out=4104, page_elems=2048, n_tokens=33,
          n_segments=0, rank_choices=(16, 24), n_adapters=3),
+    # rows of 4097..5120 elements: a second, partial shrink batch, with page chunks
+    # uniform over a 512-element slice (P = 512) and not (P = 768)
+    dict(seed=107, d_in=4608, d_out=520, page_elems=512, n_tokens=40, n_segments=1,
+         rank_choices=(8, 16, 40), n_adapters=4),
+    dict(seed=108, dtype="bf16", d_in=5120, d_out=256, page_elems=768, n_tokens=29,
+         n_segments=0, rank_choices=(3, 64), n_adapters=3),
 ]
 
 
