@@ -39,6 +39,17 @@ MUTATIONS = {
                        "if (t >= seg_offsets[s] && t <= seg_offsets[s + 1]) return seg_adapter[s];"),
     "decode_token_offset": ("return token_adapter[t - seg_end];", "return token_adapter[t - seg_end + (seg_end > 0)];"),
     "rank0_not_idle": ("if (r == 0) {", "if (r < 0) {"),
+    "shrink_rank_short": ("for (int32_t k = 0; k < r; ++k) {\n      double acc = 0.0;\n      for (int32_t j",
+                          "for (int32_t k = 0; k < r - 1; ++k) {\n      double acc = 0.0;\n      for (int32_t j"),
+    "shrink_d_in_short": ("for (int32_t j = 0; j < J->d_in; ++j) {", "for (int32_t j = 0; j < J->d_in - 1; ++j) {"),
+    "expand_d_out_short": ("for (int32_t n = 0; n < J->d_out; ++n) {\n      double acc",
+                           "for (int32_t n = 0; n < J->d_out - 1; ++n) {\n      double acc"),
+    # the previous token's row (stays inside the buffers)
+    "x_row_of_other_token": ("const uint16_t* xrow = J->x + t * (int64_t)J->d_in;",
+                             "const uint16_t* xrow = J->x + (t > 0 ? t - 1 : t) * (int64_t)J->d_in;"),
+    "y0_row_of_other_token": ("const uint16_t* y0row = J->y0 + t * (int64_t)J->d_out;",
+                              "const uint16_t* y0row = J->y0 + (t > 0 ? t - 1 : t) * (int64_t)J->d_out;"),
+    "scale_of_adapter_0": ("const double s = J->scale[i];", "const double s = J->scale[0];"),
 }
 
 
