@@ -236,7 +236,9 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
     // Per-token ids of an adapter with at least kAutoSgmvTok tokens in the call go to
     // SGMV tiles (its weights are then read once per 64 tokens instead of once per 4)
     // when SGMV runs anyway (segments) or when they are numerous enough to pay for its
-    // launches (kAutoSgmvBatch tokens); the rest to MBGMV.
+    // launches (kAutoSgmvBatch tokens); the rest to MBGMV, unless SGMV runs and fewer
+    // than kAutoMbgmvMin tokens would be left: then a launch of its own for them costs
+    // more than the tiles they add, and every id goes to SGMV.
     for (int32_t q = 0; q < n_dec; ++q) {
       const int32_t a = R->token_adapter[q];
       rc = admit(a);
@@ -244,14 +246,17 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
       if (rc == 0) continue;
       if (sc->cnt[(size_t)a]++ == 0) sc->seen.push_back(a);
     }
-    int64_t hot = 0;
+    int64_t hot = 0, cold = 0;
     for (int32_t a : sc->seen)
-      if (sc->cnt[(size_t)a] >= kAutoSgmvTok) hot += sc->cnt[(size_t)a];
-    const bool sg_hot = hot > 0 && (!sc->tiles.empty() || hot >= kAutoSgmvBatch);
+      (sc->cnt[(size_t)a] >= kAutoSgmvTok ? hot : cold) += sc->cnt[(size_t)a];
+    const bool sg_runs = !sc->tiles.empty() || hot >= kAutoSgmvBatch;
+    const bool sg_hot = hot > 0 && sg_runs;
+    const int64_t left = sg_hot ? cold : cold + hot;  // ids MBGMV would get
+    const bool sg_all = sg_runs && left > 0 && left < kAutoMbgmvMin;
     for (int32_t q = 0; q < n_dec; ++q) {
       const int32_t a = R->token_adapter[q];
       if (a < 0 || sc->cnt[(size_t)a] == 0) continue;  // no adapter, or rank 0
-      const bool to_sg = sg_hot && sc->cnt[(size_t)a] >= kAutoSgmvTok;
+      const bool to_sg = sg_all || (sg_hot && sc->cnt[(size_t)a] >= kAutoSgmvTok);
       (to_sg ? sc->sg_ad : sc->mb_ad).push_back(a);
       (to_sg ? sc->sg_in : sc->mb_in).push_back(seg_end + q);
     }

@@ -193,7 +193,7 @@ def test_validation_rejects_bad_calls():
 # ------------------------------------------------------------------ planner vs Python model
 
 MB_GROUP, SG_TILE = 4, 64
-AUTO_SGMV_TOK, AUTO_SGMV_BATCH = 4, 256
+AUTO_SGMV_TOK, AUTO_SGMV_BATCH, AUTO_MBGMV_MIN = 4, 256, 128
 
 
 def _even_split(toks, cap):
@@ -226,14 +226,19 @@ def model_plan(wl, base, policy):
     dec = [(int(a), seg_end + q) for q, a in enumerate(ta) if live(int(a))]
     if policy == _lib.POLICY_AUTO:
         # an adapter's per-token ids go to SGMV from AUTO_SGMV_TOK of them, when segments run
-        # anyway or there are at least AUTO_SGMV_BATCH such tokens
+        # anyway or there are at least AUTO_SGMV_BATCH such tokens; when SGMV runs and
+        # fewer than AUTO_MBGMV_MIN ids would be left for MBGMV, all of them go to SGMV
         cnt = {}
         for a, _ in dec:
             cnt[a] = cnt.get(a, 0) + 1
         hot = sum(c for c in cnt.values() if c >= AUTO_SGMV_TOK)
-        sg_hot = hot > 0 and (len(sg) > 0 or hot >= AUTO_SGMV_BATCH)
+        cold = sum(c for c in cnt.values() if c < AUTO_SGMV_TOK)
+        sg_runs = len(sg) > 0 or hot >= AUTO_SGMV_BATCH
+        sg_hot = hot > 0 and sg_runs
+        left = cold if sg_hot else cold + hot
+        sg_all = sg_runs and 0 < left < AUTO_MBGMV_MIN
         for a, t in dec:
-            (sg_ids if sg_hot and cnt[a] >= AUTO_SGMV_TOK else mb).append((a, t))
+            (sg_ids if sg_all or (sg_hot and cnt[a] >= AUTO_SGMV_TOK) else mb).append((a, t))
     else:
         for a, t in dec:
             (sg_ids if policy == _lib.POLICY_SGMV else mb).append((a, t))
@@ -287,7 +292,7 @@ def test_bench_accounting_follows_the_plan():
     adapter's weights once plus x, y0 and y per token."""
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     import bench
-    for name in ("decode_7b", "mlp_asym"):
+    for name in ("decode_7b", "mlp_asym", "mixed_13b"):
         wl = workloads.make(name)
         call, pool, pt, base = _call(wl)
         a = bench.algorithmic(wl, 0, call)
@@ -299,6 +304,8 @@ def test_bench_accounting_follows_the_plan():
             w = sum(int(wl.ranks[x]) for x in np.unique(routed)) * (p.d_in + p.d_out) * 2
             assert a["mbgmv_fused"]["bytes"] == w + routed.size * (p.d_in + 2 * p.d_out) * 2
             assert a["sgmv_fused"]["tokens"] == 0
-        else:  # AUTO sends the adapters with several tokens to SGMV tiles
+        elif name == "mlp_asym":  # 50 ids of adapters with < 4 tokens: too few for MBGMV
+            assert a["mbgmv_fused"]["tokens"] == 0 and a["sgmv_fused"]["tokens"] == routed.size
+        else:  # segments and hot adapters' ids on SGMV, ~360 singleton ids on MBGMV
             assert a["sgmv_fused"]["tokens"] > a["mbgmv_fused"]["tokens"] > 0
         pool.destroy()
