@@ -27,6 +27,7 @@ constexpr int kSgTile = 64;         // SGMV: tokens per tile
 constexpr int kSgSplitTiles = 64;    // SGMV: tiles of ranks <= 64 and > 64, each, for separate launches
 constexpr int kAutoSgmvTok = 4;     // AUTO: an adapter's per-token ids go to SGMV from this many
 constexpr int kAutoSgmvBatch = 256; // AUTO: ... when at least this many such tokens (or segments run)
+constexpr int kAutoSgmvShare = 4;   // ... and they are at least 1 / (1 + this) of the per-token ids
 constexpr int kAutoMbgmvMin = 128;  // AUTO: fewer per-token ids left for MBGMV join SGMV when it runs
 constexpr int kXcds = 8;            // XCDs (dies, each with its own L2) workgroups are dealt to in turn
 constexpr int kSgMaxSplit = 8;      // SGMV shrink: most k-ranges d_in is cut into

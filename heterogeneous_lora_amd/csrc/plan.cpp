@@ -236,7 +236,9 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
     // Per-token ids of an adapter with at least kAutoSgmvTok tokens in the call go to
     // SGMV tiles (its weights are then read once per 64 tokens instead of once per 4)
     // when SGMV runs anyway (segments) or when they are numerous enough to pay for its
-    // launches (kAutoSgmvBatch tokens); the rest to MBGMV, unless SGMV runs and fewer
+    // launches (kAutoSgmvBatch tokens, and at least a 1 / (1 + kAutoSgmvShare) share of
+    // the ids: a small share saves less than the launches cost); the rest to MBGMV,
+    // unless SGMV runs and fewer
     // than kAutoMbgmvMin tokens would be left: then a launch of its own for them costs
     // more than the tiles they add, and every id goes to SGMV.
     for (int32_t q = 0; q < n_dec; ++q) {
@@ -249,7 +251,8 @@ int64_t plan_bytes(const slora_lora* L, const slora_routing* R, PlanScratch* sc,
     int64_t hot = 0, cold = 0;
     for (int32_t a : sc->seen)
       (sc->cnt[(size_t)a] >= kAutoSgmvTok ? hot : cold) += sc->cnt[(size_t)a];
-    const bool sg_runs = !sc->tiles.empty() || hot >= kAutoSgmvBatch;
+    const bool sg_runs =
+        !sc->tiles.empty() || (hot >= kAutoSgmvBatch && hot * kAutoSgmvShare >= cold);
     const bool sg_hot = hot > 0 && sg_runs;
     const int64_t left = sg_hot ? cold : cold + hot;  // ids MBGMV would get
     const bool sg_all = sg_runs && left > 0 && left < kAutoMbgmvMin;

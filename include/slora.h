@@ -66,9 +66,9 @@ extern "C" {
 /* Which kernel family serves which tokens (slora_routing.policy). */
 /* AUTO: segment tokens -> SGMV (MFMA); per-token ids -> MBGMV, except that the ids of an
  * adapter with 4 or more of them in the call go to SGMV when SGMV runs anyway (segments)
- * or there are at least 256 such ids, and that all ids go to SGMV when it runs and fewer
- * than 128 would be left for MBGMV. The routing changes which kernels run, not results
- * beyond rounding. */
+ * or there are at least 256 such ids making at least a fifth of all per-token ids, and
+ * that all ids go to SGMV when it runs and fewer than 128 would be left for MBGMV. The
+ * routing changes which kernels run, not results beyond rounding. */
 #define SLORA_POLICY_AUTO 0
 #define SLORA_POLICY_MBGMV 1 /* every routed token -> MBGMV (segments grouped like ids) */
 #define SLORA_POLICY_SGMV 2  /* every routed token -> SGMV (ids bucketed by adapter) */

@@ -193,7 +193,7 @@ def test_validation_rejects_bad_calls():
 # ------------------------------------------------------------------ planner vs Python model
 
 MB_GROUP, SG_TILE = 4, 64
-AUTO_SGMV_TOK, AUTO_SGMV_BATCH, AUTO_MBGMV_MIN = 4, 256, 128
+AUTO_SGMV_TOK, AUTO_SGMV_BATCH, AUTO_MBGMV_MIN, AUTO_SGMV_SHARE = 4, 256, 128, 4
 
 
 def _even_split(toks, cap):
@@ -226,14 +226,15 @@ def model_plan(wl, base, policy):
     dec = [(int(a), seg_end + q) for q, a in enumerate(ta) if live(int(a))]
     if policy == _lib.POLICY_AUTO:
         # an adapter's per-token ids go to SGMV from AUTO_SGMV_TOK of them, when segments run
-        # anyway or there are at least AUTO_SGMV_BATCH such tokens; when SGMV runs and
+        # anyway or there are at least AUTO_SGMV_BATCH such tokens (and at least a fifth of
+        # the ids); when SGMV runs and
         # fewer than AUTO_MBGMV_MIN ids would be left for MBGMV, all of them go to SGMV
         cnt = {}
         for a, _ in dec:
             cnt[a] = cnt.get(a, 0) + 1
         hot = sum(c for c in cnt.values() if c >= AUTO_SGMV_TOK)
         cold = sum(c for c in cnt.values() if c < AUTO_SGMV_TOK)
-        sg_runs = len(sg) > 0 or hot >= AUTO_SGMV_BATCH
+        sg_runs = len(sg) > 0 or (hot >= AUTO_SGMV_BATCH and hot * AUTO_SGMV_SHARE >= cold)
         sg_hot = hot > 0 and sg_runs
         left = cold if sg_hot else cold + hot
         sg_all = sg_runs and 0 < left < AUTO_MBGMV_MIN
