@@ -12,6 +12,7 @@
 #include <map>
 #include <mutex>
 
+#include "guard.h"
 #include "internal.h"
 
 using namespace slora;
@@ -302,14 +303,14 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
 
 extern "C" {
 
-int slora_timing_enable(int32_t on) {
+static int impl_slora_timing_enable(int32_t on) {
   clear_error();
   std::lock_guard<std::mutex> lk(g_mu);
   g_timing_on = on != 0;
   return SLORA_OK;
 }
 
-int slora_timing_read(int32_t n_kernels, int64_t* launches, double* total_ms) {
+static int impl_slora_timing_read(int32_t n_kernels, int64_t* launches, double* total_ms) {
   clear_error();
   if (n_kernels < 0 || n_kernels > SLORA_K_COUNT || (n_kernels > 0 && (!launches || !total_ms)))
     return fail(SLORA_E_INVALID, "timing_read: bad arguments");
@@ -331,14 +332,14 @@ int slora_timing_read(int32_t n_kernels, int64_t* launches, double* total_ms) {
   return rc;
 }
 
-int slora_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes) {
+static int impl_slora_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes) {
   clear_error();
   if (!lora || !routing || !bytes) return fail(SLORA_E_INVALID, "workspace_size: NULL argument");
   *bytes = ws_layout(lora, routing).total;
   return SLORA_OK;
 }
 
-int slora_workspace_status(const void* ws, void* stream, int32_t* status) {
+static int impl_slora_workspace_status(const void* ws, void* stream, int32_t* status) {
   clear_error();
   if (!ws || !status) return fail(SLORA_E_INVALID, "workspace_status: NULL argument");
   unsigned long long flag = 0;
@@ -351,22 +352,22 @@ int slora_workspace_status(const void* ws, void* stream, int32_t* status) {
   return SLORA_OK;
 }
 
-int slora_shrink(const slora_lora* lora, const slora_routing* routing, const void* x, float* v,
+static int impl_slora_shrink(const slora_lora* lora, const slora_routing* routing, const void* x, float* v,
                  void* ws, int64_t ws_bytes, void* stream) {
   return run(lora, routing, x, v, nullptr, nullptr, ws, ws_bytes, stream, kShrink);
 }
 
-int slora_expand(const slora_lora* lora, const slora_routing* routing, const float* v, void* y,
+static int impl_slora_expand(const slora_lora* lora, const slora_routing* routing, const float* v, void* y,
                  void* ws, int64_t ws_bytes, void* stream) {
   return run(lora, routing, nullptr, nullptr, v, y, ws, ws_bytes, stream, kExpand);
 }
 
-int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
+static int impl_slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
                 void* ws, int64_t ws_bytes, void* stream) {
   return run(lora, routing, x, nullptr, nullptr, y, ws, ws_bytes, stream, kApply);
 }
 
-int slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int32_t* n_groups,
+static int impl_slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int32_t* n_groups,
                        int32_t* info, int32_t info_cap, int32_t* tokens) {
   clear_error();
   if (!n_groups) return fail(SLORA_E_INVALID, "plan_inspect: n_groups is NULL");
@@ -409,6 +410,48 @@ int slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int
     ++at;
   }
   return SLORA_OK;
+}
+
+}  // extern "C"
+
+// Entry points: every C++ exception (host memory exhausted included) becomes an
+// error code here, so none crosses the C ABI.
+extern "C" {
+
+int slora_timing_enable(int32_t on) {
+  return slora::guarded(__func__, [&] { return impl_slora_timing_enable(on); });
+}
+
+int slora_timing_read(int32_t n_kernels, int64_t* launches, double* total_ms) {
+  return slora::guarded(__func__, [&] { return impl_slora_timing_read(n_kernels, launches, total_ms); });
+}
+
+int slora_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes) {
+  return slora::guarded(__func__, [&] { return impl_slora_workspace_size(lora, routing, bytes); });
+}
+
+int slora_workspace_status(const void* ws, void* stream, int32_t* status) {
+  return slora::guarded(__func__, [&] { return impl_slora_workspace_status(ws, stream, status); });
+}
+
+int slora_shrink(const slora_lora* lora, const slora_routing* routing, const void* x, float* v,
+                 void* ws, int64_t ws_bytes, void* stream) {
+  return slora::guarded(__func__, [&] { return impl_slora_shrink(lora, routing, x, v, ws, ws_bytes, stream); });
+}
+
+int slora_expand(const slora_lora* lora, const slora_routing* routing, const float* v, void* y,
+                 void* ws, int64_t ws_bytes, void* stream) {
+  return slora::guarded(__func__, [&] { return impl_slora_expand(lora, routing, v, y, ws, ws_bytes, stream); });
+}
+
+int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
+                void* ws, int64_t ws_bytes, void* stream) {
+  return slora::guarded(__func__, [&] { return impl_slora_apply(lora, routing, x, y, ws, ws_bytes, stream); });
+}
+
+int slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int32_t* n_groups,
+                       int32_t* info, int32_t info_cap, int32_t* tokens) {
+  return slora::guarded(__func__, [&] { return impl_slora_plan_inspect(lora, routing, n_groups, info, info_cap, tokens); });
 }
 
 }  // extern "C"

@@ -16,6 +16,7 @@
 #include <map>
 #include <mutex>
 
+#include "guard.h"
 #include "internal.h"
 
 namespace slora {
@@ -28,7 +29,10 @@ int fail(int code, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  t_error = buf;
+  try {
+    t_error = buf;
+  } catch (...) {  // no message rather than an exception across the C ABI
+  }
   return code;
 }
 
@@ -90,7 +94,7 @@ const char* slora_last_error(void) { return t_error.c_str(); }
 
 int slora_abi_version(void) { return SLORA_ABI_VERSION; }
 
-int slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
+static int impl_slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
                       uint64_t shuffle_seed, slora_pool** out) {
   clear_error();
   if (!out) return fail(SLORA_E_INVALID, "pool_create: out is NULL");
@@ -123,7 +127,7 @@ int slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page_elems, int3
   return SLORA_OK;
 }
 
-int slora_pool_destroy(slora_pool* pool) {
+static int impl_slora_pool_destroy(slora_pool* pool) {
   clear_error();
   if (!pool) return SLORA_OK;
   int rc = SLORA_OK;
@@ -141,7 +145,7 @@ int slora_pool_destroy(slora_pool* pool) {
   return rc;
 }
 
-int slora_pool_info(const slora_pool* pool, int64_t* n_pages, int64_t* n_free, int32_t* page_elems,
+static int impl_slora_pool_info(const slora_pool* pool, int64_t* n_pages, int64_t* n_free, int32_t* page_elems,
                     int32_t* dtype) {
   clear_error();
   if (!pool) return fail(SLORA_E_INVALID, "pool_info: pool is NULL");
@@ -152,7 +156,7 @@ int slora_pool_info(const slora_pool* pool, int64_t* n_pages, int64_t* n_free, i
   return SLORA_OK;
 }
 
-int slora_pool_alloc_kv(slora_pool* pool, int32_t n, int32_t* out_page_ids) {
+static int impl_slora_pool_alloc_kv(slora_pool* pool, int32_t n, int32_t* out_page_ids) {
   clear_error();
   if (!pool) return fail(SLORA_E_INVALID, "alloc_kv: pool is NULL");
   if (n < 0) return fail(SLORA_E_INVALID, "alloc_kv: n < 0");
@@ -169,7 +173,7 @@ int slora_pool_alloc_kv(slora_pool* pool, int32_t n, int32_t* out_page_ids) {
   return SLORA_OK;
 }
 
-int slora_pool_free_kv(slora_pool* pool, const int32_t* page_ids, int32_t n) {
+static int impl_slora_pool_free_kv(slora_pool* pool, const int32_t* page_ids, int32_t n) {
   clear_error();
   if (!pool) return fail(SLORA_E_INVALID, "free_kv: pool is NULL");
   if (n < 0 || (n > 0 && !page_ids)) return fail(SLORA_E_INVALID, "free_kv: bad page list");
@@ -190,7 +194,7 @@ int slora_pool_free_kv(slora_pool* pool, const int32_t* page_ids, int32_t n) {
   return SLORA_OK;
 }
 
-int slora_pool_alloc_adapter(slora_pool* pool, int32_t adapter_id, int32_t rank, int32_t n_proj,
+static int impl_slora_pool_alloc_adapter(slora_pool* pool, int32_t adapter_id, int32_t rank, int32_t n_proj,
                              const int32_t* d_in, const int32_t* d_out) {
   clear_error();
   if (!pool) return fail(SLORA_E_INVALID, "alloc_adapter: pool is NULL");
@@ -233,7 +237,7 @@ int slora_pool_alloc_adapter(slora_pool* pool, int32_t adapter_id, int32_t rank,
   return SLORA_OK;
 }
 
-int slora_pool_free_adapter(slora_pool* pool, int32_t adapter_id) {
+static int impl_slora_pool_free_adapter(slora_pool* pool, int32_t adapter_id) {
   clear_error();
   if (!pool) return fail(SLORA_E_INVALID, "free_adapter: pool is NULL");
   auto it = pool->adapters.find(adapter_id);
@@ -257,7 +261,7 @@ int slora_pool_free_adapter(slora_pool* pool, int32_t adapter_id) {
   return SLORA_OK;
 }
 
-int slora_pool_page_table(const slora_pool* pool, int32_t proj, int32_t n_adapters, int32_t* pt,
+static int impl_slora_pool_page_table(const slora_pool* pool, int32_t proj, int32_t n_adapters, int32_t* pt,
                           int64_t pt_cap, int64_t* pt_len, int64_t* base, int32_t* rank) {
   clear_error();
   if (!pool) return fail(SLORA_E_INVALID, "page_table: pool is NULL");
@@ -296,7 +300,7 @@ int slora_pool_page_table(const slora_pool* pool, int32_t proj, int32_t n_adapte
   return SLORA_OK;
 }
 
-int slora_pool_owners(const slora_pool* pool, int32_t* owner) {
+static int impl_slora_pool_owners(const slora_pool* pool, int32_t* owner) {
   clear_error();
   if (!pool || !owner) return fail(SLORA_E_INVALID, "pool_owners: NULL argument");
   memcpy(owner, pool->owner.data(), pool->owner.size() * sizeof(int32_t));
@@ -324,7 +328,7 @@ static int device_view(const void* host, const void** dev, const char* what) {
   return SLORA_OK;
 }
 
-int slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
+static int impl_slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
                       const void* const* host_B, void* side_stream, void* done_event) {
   clear_error();
   if (!pool) return fail(SLORA_E_INVALID, "fetch: pool is NULL");
@@ -381,6 +385,57 @@ int slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* h
     if (e != hipSuccess) return hip_fail(e, "fetch: hipEventRecord(done)");
   }
   return SLORA_OK;
+}
+
+}  // extern "C"
+
+// Entry points: every C++ exception (host memory exhausted included) becomes an
+// error code here, so none crosses the C ABI.
+extern "C" {
+
+int slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
+                      uint64_t shuffle_seed, slora_pool** out) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_create(dev_pages, n_pages, page_elems, dtype, shuffle_seed, out); });
+}
+
+int slora_pool_destroy(slora_pool* pool) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_destroy(pool); });
+}
+
+int slora_pool_info(const slora_pool* pool, int64_t* n_pages, int64_t* n_free, int32_t* page_elems,
+                    int32_t* dtype) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_info(pool, n_pages, n_free, page_elems, dtype); });
+}
+
+int slora_pool_alloc_kv(slora_pool* pool, int32_t n, int32_t* out_page_ids) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_alloc_kv(pool, n, out_page_ids); });
+}
+
+int slora_pool_free_kv(slora_pool* pool, const int32_t* page_ids, int32_t n) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_free_kv(pool, page_ids, n); });
+}
+
+int slora_pool_alloc_adapter(slora_pool* pool, int32_t adapter_id, int32_t rank, int32_t n_proj,
+                             const int32_t* d_in, const int32_t* d_out) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_alloc_adapter(pool, adapter_id, rank, n_proj, d_in, d_out); });
+}
+
+int slora_pool_free_adapter(slora_pool* pool, int32_t adapter_id) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_free_adapter(pool, adapter_id); });
+}
+
+int slora_pool_page_table(const slora_pool* pool, int32_t proj, int32_t n_adapters, int32_t* pt,
+                          int64_t pt_cap, int64_t* pt_len, int64_t* base, int32_t* rank) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_page_table(pool, proj, n_adapters, pt, pt_cap, pt_len, base, rank); });
+}
+
+int slora_pool_owners(const slora_pool* pool, int32_t* owner) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_owners(pool, owner); });
+}
+
+int slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
+                      const void* const* host_B, void* side_stream, void* done_event) {
+  return slora::guarded(__func__, [&] { return impl_slora_fetch_async(pool, adapter_id, host_AT, host_B, side_stream, done_event); });
 }
 
 }  // extern "C"
