@@ -38,7 +38,9 @@
  *
  * Errors. Every call returns SLORA_OK (0) or a negative code; slora_last_error()
  * returns a thread-local message for the last failure on the calling thread.
- * A failing call changes nothing (allocation is all-or-nothing).
+ * A failing call changes nothing (allocation is all-or-nothing). No C++ exception
+ * leaves the library: host memory running out inside a call is SLORA_E_INVALID
+ * with a message saying so.
  *
  * Threads. A pool handle is not thread-safe: one owner at a time. Compute calls
  * may run from several threads on different streams.
@@ -55,7 +57,7 @@ extern "C" {
 #define SLORA_ABI_VERSION 1
 
 #define SLORA_OK 0
-#define SLORA_E_INVALID (-1)   /* bad argument, shape, alignment or routing */
+#define SLORA_E_INVALID (-1)   /* bad argument, shape, alignment or routing; host memory exhausted */
 #define SLORA_E_POOL_FULL (-2) /* not enough free pages; nothing was allocated */
 #define SLORA_E_STATE (-3)     /* adapter absent / already resident / fetch in flight */
 #define SLORA_E_HIP (-4)       /* a HIP runtime call failed */
