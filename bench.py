@@ -11,9 +11,15 @@ Steps rotate over --instances independent copies of the workload (own pool, own
 pages, own x / y), about 0.5 GiB each, so the 256 MB Infinity Cache cannot hold
 the weights of the instance being timed: the kernels read adapter pages from HBM.
 
-Printed: one JSON line on stdout (tokens/s, roofline of the dominant kernel from
-HIP events around its launches, the CPU oracle's rate on the host cores, fetch
-rate). Progress goes to stderr.
+Printed: one JSON line on stdout: tokens/s, the roofline of the dominant kernel
+from HIP events the launches record (with p10/p50/p90 of its launch durations), a
+plain device copy as a reachable-bandwidth reference, the CPU oracle's rate on the
+host cores, the adapter fetch rate beside a copy-engine host-to-device copy of the
+same bytes, and GPU / host facts. With the default decode workload the same line
+carries a `prefill` record: the prefill SGMV batch (64 requests, q/k/v/o 4096 ->
+4096, bf16) timed the same way, with HBM and MFMA fractions of both SGMV kernels.
+Every instance's workspace status is read after the timed steps; a decode launch
+whose wait gave up makes the run exit with status 3. Progress goes to stderr.
 """
 
 from __future__ import annotations
@@ -146,43 +152,260 @@ def pmc_summary(a):
     print(json.dumps(out))
 
 
-def cpu_baseline(wl, budget_s):
+def oracle_threads():
+    """Threads the oracle baseline runs on: every core this process may use, capped at the
+    CPU share one job gets on the GPU host (16 cores per GPU; OMP_NUM_THREADS says so there)."""
+    aff = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    return max(1, min(aff, share)), aff
+
+
+def cpu_baseline(wl, budget_s, threads=None, single_thread_s=0.0):
     """The oracle (fp64 C loops, threads over tokens) on the host cores, on the same
-    workload: full steps while they fit the budget, else a token sample."""
+    workload: full steps while they fit the budget, else a token sample. With
+    single_thread_s > 0, also one thread alone on a token sample for about that long."""
     import oracle
-    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-    prepared = []
+    if threads is None:
+        threads, aff = oracle_threads()
+    else:
+        aff = len(os.sched_getaffinity(0))
     T = wl.n_tokens
-    # a token sample when one full step would not fit the budget (cost ~ rank * (d_in + d_out))
     ids = np.concatenate([np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets)), wl.token_adapter])
     work = sum(int(wl.ranks[a]) * (p.d_in + p.d_out) for a in ids if a >= 0 for p in wl.projections)
-    est_s = work / (1.5e8 * threads)
-    n_eval = T if est_s < budget_s / 4 else max(16, int(T * (budget_s / 4) / est_s))
-    ev = np.sort(np.random.default_rng(0).choice(T, size=n_eval, replace=False)) if n_eval < T else None
-    for proj in range(len(wl.projections)):
-        p = wl.projections[proj]
-        need = sorted(set(int(a) for a in (ids if ev is None else ids[ev]) if a >= 0 and wl.ranks[a] > 0))
-        adapters = {a: wl.adapter(a, proj) for a in need}
-        pool, pt, base = oracle.build_pool(adapters, wl.n_adapters, p.d_in, p.d_out,
-                                           wl.page_elems, wl.dtype, np.random.default_rng(proj))
-        prepared.append(dict(dtype=wl.dtype, d_in=p.d_in, d_out=p.d_out, x=wl.x(proj),
-                             y0=wl.y0(proj), pool=pool, page_elems=wl.page_elems, page_table=pt,
-                             base=base, rank=wl.ranks, scale=wl.scales, seg_offsets=wl.seg_offsets,
-                             seg_adapter=wl.seg_adapter, token_adapter=wl.token_adapter,
-                             eval_tokens=ev, n_threads=threads))
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for kw in prepared:
-            oracle.lora(**kw)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 10000:
-            break
-    tokens = reps * (T if ev is None else ev.size)
-    sample = (f"{reps} full steps ({T} tokens x {len(wl.projections)} projections)" if ev is None
-              else f"{reps} x {ev.size} of {T} tokens (seeded sample) x {len(wl.projections)} projections")
-    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(el, 3)}
+
+    def prepare(n_threads, budget):
+        # a token sample when one full step would not fit the budget (cost ~ rank * (d_in + d_out))
+        est_s = work / (1.5e8 * n_threads)
+        n_eval = T if est_s < budget / 4 else max(16, int(T * (budget / 4) / est_s))
+        ev = np.sort(np.random.default_rng(0).choice(T, size=n_eval, replace=False)) if n_eval < T else None
+        prepared = []
+        for proj in range(len(wl.projections)):
+            p = wl.projections[proj]
+            need = sorted(set(int(a) for a in (ids if ev is None else ids[ev]) if a >= 0 and wl.ranks[a] > 0))
+            adapters = {a: wl.adapter(a, proj) for a in need}
+            pool, pt, base = oracle.build_pool(adapters, wl.n_adapters, p.d_in, p.d_out,
+                                               wl.page_elems, wl.dtype, np.random.default_rng(proj))
+            prepared.append(dict(dtype=wl.dtype, d_in=p.d_in, d_out=p.d_out, x=wl.x(proj),
+                                 y0=wl.y0(proj), pool=pool, page_elems=wl.page_elems, page_table=pt,
+                                 base=base, rank=wl.ranks, scale=wl.scales, seg_offsets=wl.seg_offsets,
+                                 seg_adapter=wl.seg_adapter, token_adapter=wl.token_adapter,
+                                 eval_tokens=ev, n_threads=n_threads))
+        return prepared, ev
+
+    def timed(prepared, ev, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for kw in prepared:
+                oracle.lora(**kw)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 10000:
+                break
+        n = T if ev is None else ev.size
+        sample = (f"{reps} full steps ({T} tokens x {len(wl.projections)} projections)" if ev is None
+                  else f"{reps} x {ev.size} of {T} tokens (seeded sample) x {len(wl.projections)} projections")
+        return reps * n / el, sample, el
+
+    prepared, ev = prepare(threads, budget_s)
+    value, sample, el = timed(prepared, ev, budget_s)
+    out = {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": sample, "seconds": round(el, 3), "host_affinity_cores": aff,
+           "cpu_model": cpu_model()}
+    if single_thread_s > 0:
+        prepared, ev = prepare(1, single_thread_s)
+        v1, s1, e1 = timed(prepared, ev, single_thread_s)
+        out["single_thread"] = {"value": v1, "unit": "tokens/s", "cores": 1, "sample": s1,
+                                "seconds": round(e1, 3)}
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def device_info():
+    """GPU name, CU count, peak engine and memory clocks (hipDeviceGetAttribute through the
+    HIP runtime torch loaded), ROCm / torch versions."""
+    import ctypes
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    info = {"gpu": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+            "hip_runtime": torch.version.hip, "torch": torch.__version__}
+    try:
+        hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        for key, attr in (("sclk_peak_mhz", 5), ("mclk_peak_mhz", 60)):  # ClockRate, MemoryClockRate (kHz)
+            v = ctypes.c_int(0)
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0:
+                info[key] = v.value // 1000
+    except OSError:
+        pass
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    return info
+
+
+def copy_reference(dev, nbytes=256 << 20, reps=10):
+    """A plain device-to-device copy of nbytes (torch's copy kernel), timed with events on the
+    current stream: GB/s counting the bytes read and written (2 * nbytes per copy)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    return {"bytes": nbytes, "ms": round(ms, 4), "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def h2d_reference(dev, nbytes, reps=5):
+    """Copy-engine host-to-device rate: nbytes from pinned host memory (hipMemcpyAsync)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    return {"bytes": nbytes, "ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+
+
+def pct(a, q):
+    return round(float(np.percentile(np.asarray(a), q)), 3) if len(a) else None
+
+
+def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev):
+    """Time `steps` steps (one apply per projection, rotating over n_inst instances) after
+    `warmup` untimed ones. Returns the measured figures; exits non-zero if a fused call's
+    wait gave up in any of them (its results would not be valid)."""
+    import torch
+    from heterogeneous_lora_amd import _lib, runtime
+    T = wl.n_tokens
+    n_proj = len(wl.projections)
+    active = [int(a) for a in wl.active_adapters()]
+    log(f"[bench] {wl.name}: {wl.description}")
+    log(f"[bench] {T} tokens, {len(active)} active adapters, {n_proj} projection(s), {n_inst} instance(s)")
+    store = runtime.HostStore(wl, active)
+    host_io = [(wl.x(p), wl.y0(p)) for p in range(n_proj)]
+    insts, fetch_ms = [], []
+    for i in range(n_inst):
+        inst = runtime.PagedLoRA(wl, device=dev, store=store, pool_seed=wl.pool_seed + i)
+        fetch_ms.append(inst.fetch_ms)
+        calls = [inst.call(p, policy) for p in range(n_proj)]
+        io = [(runtime._dev_i16(x, inst.device), runtime._dev_i16(y0, inst.device)) for x, y0 in host_io]
+        ws = torch.zeros(max(_lib.workspace_size(c) for c in calls), dtype=torch.uint8, device=dev)
+        insts.append((inst, calls, io, ws))
+        log(f"[bench] instance {i} ready (fetch {inst.fetch_ms:.2f} ms)")
+    del host_io
+    fetch_bytes = sum(int(wl.ranks[a]) * (p.d_in + p.d_out) * 2 for a in active for p in wl.projections)
+
+    stream = torch.cuda.current_stream(dev)
+    bound = [[inst.bind_apply(calls[p], io[p][0], io[p][1], ws, stream) for p in range(n_proj)]
+             for inst, calls, io, ws in insts]
+
+    def step(i):
+        for run in bound[i % len(bound)]:
+            run()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    _lib.timing_enable(True)  # creates the event pairs the timed launches use
+    _lib.timing_enable(False)
+    _lib.timing_read_all()  # start from an empty record
+    # HIP events recorded by the launch itself bracket every kernel of one step in
+    # `event_every` (recording costs the host a few microseconds per launch, which would
+    # otherwise pace the loop)
+    ev = max(1, event_every)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if i % ev == 0:
+            _lib.timing_enable(True)
+            step(i)
+            _lib.timing_enable(False)
+        else:
+            step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    names, ms = _lib.timing_read_all()
+    wall = t1 - t0
+    # then pct_steps more steps with every launch timed, for the spread of kernel durations
+    _lib.timing_enable(True)
+    for i in range(pct_steps):
+        step(i)
+    _lib.timing_enable(False)
+    torch.cuda.synchronize()
+    pnames, pms = _lib.timing_read_all()
+    bad = [i for i, (_, _, _, ws) in enumerate(insts) if _lib.workspace_status(ws.data_ptr(), stream.cuda_stream)]
+    if bad:
+        print(f"bench.py: a decode launch gave up waiting in instance(s) {bad}: results invalid",
+              file=sys.stderr)
+        sys.exit(3)
+
+    ms_per_step = wall / steps * 1e3
+    value = T * steps / wall
+    log(f"[bench] {steps} steps in {wall:.4f} s: {ms_per_step * 1e3:.1f} us/step, {value:.4g} tokens/s")
+    alg = [algorithmic(wl, p, insts[0][1][p]) for p in range(n_proj)]
+    kernels = {}
+    for k in sorted(set(names)):
+        d = np.array([m for n, m in zip(names, ms) if n == k])
+        dp = np.array([m for n, m in zip(pnames, pms) if n == k]) * 1e3
+        per_launch_bytes = float(np.mean([a[k]["bytes"] for a in alg]))
+        per_launch_flops = float(np.mean([a[k]["flops"] for a in alg]))
+        avg_s = float(d.mean()) * 1e-3
+        kernels[k] = {"launches": int(d.size), "avg_us": round(avg_s * 1e6, 3),
+                      "p10_us": pct(dp, 10), "p50_us": pct(dp, 50), "p90_us": pct(dp, 90),
+                      "pct_launches": int(dp.size),
+                      "algorithmic_bytes": int(per_launch_bytes),
+                      "gbps": round(per_launch_bytes / avg_s / 1e9, 1),
+                      "tflops": round(per_launch_flops / avg_s / 1e12, 3)}
+    n_timed = (steps + ev - 1) // ev
+    kern_total_s = float(np.sum(ms)) * 1e-3 / n_timed
+    step_bytes = sum(kv["algorithmic_bytes"] * kv["launches"] for kv in kernels.values()) / n_timed
+    log(f"[bench] kernels: {json.dumps(kernels)}")
+    log(f"[bench] all kernels of a step: {kern_total_s * 1e6:.1f} us, "
+        f"{step_bytes / kern_total_s / 1e9:.0f} GB/s algorithmic")
+    fms = float(np.median(fetch_ms))
+    out = dict(value=value, ms_per_step=ms_per_step, kernels=kernels, event_every=ev,
+               step_kernel_us=round(kern_total_s * 1e6, 2),
+               step_algorithmic_gbps=round(step_bytes / kern_total_s / 1e9, 1),
+               fetch={"bytes": fetch_bytes, "ms": round(fms, 3),
+                      "gbps": round(fetch_bytes / (fms * 1e-3) / 1e9, 2)},
+               active=len(active), workspace_status="clean")
+    for inst, *_ in insts:
+        inst.close()
+    return out
+
+
+def roofline_of(kernels, workload, kernel=None):
+    dom = kernel or max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    dk = kernels[dom]
+    r = {"bound": "hbm", "kernel": dom, "achieved": dk["gbps"], "peak": HBM_PEAK_GBPS,
+         "unit": "GB/s", "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4),
+         "traffic": load_traffic(dom, workload)}
+    if dom.startswith("sgmv"):
+        r["mfma_tflops"] = dk["tflops"]
+        r["mfma_frac"] = round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
+    return r
 
 
 def main():
@@ -197,6 +420,10 @@ def main():
     ap.add_argument("--instances", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode_7b only: skip the prefill_sgmv sub-record")
+    ap.add_argument("--pct-steps", type=int, default=64,
+                    help="extra steps, every launch timed, for the p10/p50/p90 kernel durations")
     ap.add_argument("--event-every", type=int, default=4,
                     help="time the kernels of one step in this many with HIP events")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
@@ -222,122 +449,71 @@ def main():
 
     import torch
     import workloads
-    from heterogeneous_lora_amd import _lib, runtime
+    from heterogeneous_lora_amd import _lib
 
     _lib.load()
     policy = {"auto": 0, "mbgmv": 1, "sgmv": 2}[args.policy]
     wl = workloads.make(args.config, **({"n_active": args.active} if args.active else {}))
-    T = wl.n_tokens
-    n_proj = len(wl.projections)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"[bench] {wl.name}: {wl.description}")
-    active = [int(a) for a in wl.active_adapters()]
-    log(f"[bench] {T} tokens, {len(active)} active adapters, {n_proj} projection(s)")
+    dinfo = device_info()
+    log(f"[bench] device: {dinfo}")
+    main_run = run_workload(wl, policy, args.instances, args.steps, args.warmup, args.event_every,
+                            args.pct_steps, dev)
+    roofline = roofline_of(main_run["kernels"], wl.name)
+    copy_ref = copy_reference(dev)
+    roofline["copy_gbps"] = copy_ref["gbps"]
+    roofline["frac_of_copy"] = round(roofline["achieved"] / copy_ref["gbps"], 4)
+    fetch = dict(main_run["fetch"])
+    h2d = h2d_reference(dev, fetch["bytes"])
+    fetch["h2d_copy_engine_gbps"] = h2d["gbps"]
+    fetch["frac_of_h2d"] = round(fetch["gbps"] / h2d["gbps"], 4)
 
-    store = runtime.HostStore(wl, active)
-    insts, fetch_ms = [], []
-    for i in range(args.instances):
-        inst = runtime.PagedLoRA(wl, device="cuda:0", store=store, pool_seed=wl.pool_seed + i)
-        fetch_ms.append(inst.fetch_ms)
-        calls = [inst.call(p, policy) for p in range(n_proj)]
-        io = [inst.inputs(p) for p in range(n_proj)]
-        ws = torch.zeros(max(_lib.workspace_size(c) for c in calls), dtype=torch.uint8, device=dev)
-        insts.append((inst, calls, io, ws))
-        log(f"[bench] instance {i} ready (fetch {inst.fetch_ms:.2f} ms)")
-    fetch_bytes = sum(int(wl.ranks[a]) * (p.d_in + p.d_out) * 2 for a in active
-                      for p in wl.projections)
-
-    stream = torch.cuda.current_stream(dev)
-    # per instance and projection, the apply call with its arguments marshalled once
-    bound = [[inst.bind_apply(calls[p], io[p][0], io[p][1], ws, stream) for p in range(n_proj)]
-             for inst, calls, io, ws in insts]
-
-    def step(i):
-        for run in bound[i % len(bound)]:
-            run()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    _lib.timing_read()  # start from empty kernel counters
-    # HIP events bracket every kernel of one step in `event_every` (recording them costs
-    # the host a few microseconds per launch, which would otherwise pace the loop)
-    ev = max(1, args.event_every)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i % ev == 0:
-            _lib.timing_enable(True)
-            step(i)
-            _lib.timing_enable(False)
-        else:
-            step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    timing = _lib.timing_read()
-    _lib.timing_enable(False)
-    wall = t1 - t0
-    ms_per_step = wall / args.steps * 1e3
-    value = T * args.steps / wall
-    log(f"[bench] {args.steps} steps in {wall:.4f} s: {ms_per_step * 1e3:.1f} us/step, "
-        f"{value:.4g} tokens/s")
-
-    # per-kernel roofline (bytes and flops averaged over the projections' launches)
-    alg = [algorithmic(wl, p, insts[0][1][p]) for p in range(n_proj)]
-    kernels = {}
-    for k, (n, ms) in timing.items():
-        if n == 0:
-            continue
-        per_launch_bytes = float(np.mean([a[k]["bytes"] for a in alg]))
-        per_launch_flops = float(np.mean([a[k]["flops"] for a in alg]))
-        avg_s = ms / n * 1e-3
-        kernels[k] = {"launches": n, "avg_us": round(avg_s * 1e6, 3),
-                      "algorithmic_bytes": int(per_launch_bytes),
-                      "gbps": round(per_launch_bytes / avg_s / 1e9, 1),
-                      "tflops": round(per_launch_flops / avg_s / 1e12, 3)}
-    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
-    dk = kernels[dom]
-    sgmv_like = dom.startswith("sgmv")
-    traffic = load_traffic(dom, wl.name)
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["gbps"], "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic}
-    if sgmv_like:
-        roofline["mfma_frac"] = round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
-    n_timed = (args.steps + ev - 1) // ev
-    kern_total_s = sum(ms for n, ms in timing.values()) * 1e-3 / n_timed
-    step_bytes = sum(kv["algorithmic_bytes"] * kv["launches"] for kv in kernels.values()) / n_timed
-    log(f"[bench] kernels: {json.dumps(kernels)}")
-    log(f"[bench] all kernels of a step: {kern_total_s * 1e6:.1f} us, "
-        f"{step_bytes / kern_total_s / 1e9:.0f} GB/s algorithmic")
+    prefill = None
+    if args.config == "decode_7b" and not args.no_prefill:
+        pw = workloads.make("prefill_sgmv")
+        pr = run_workload(pw, 0, 2, max(10, min(args.steps, 40)), max(2, min(args.warmup, 5)),
+                          args.event_every, min(args.pct_steps, 16), dev)
+        prefill = {"workload": pw.name, "value": round(pr["value"], 1), "unit": "tokens/s",
+                   "ms_per_step": round(pr["ms_per_step"], 5), "tokens": pw.n_tokens,
+                   "projections": len(pw.projections), "instances_rotated": 2,
+                   "kernels": pr["kernels"], "step_kernel_us": pr["step_kernel_us"],
+                   "step_algorithmic_gbps": pr["step_algorithmic_gbps"],
+                   "roofline": {k: roofline_of(pr["kernels"], pw.name, k)
+                                for k in ("sgmv_shrink", "sgmv_expand") if k in pr["kernels"]},
+                   "workspace_status": pr["workspace_status"]}
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds,
+                           single_thread_s=min(3.0, args.cpu_seconds) if wl.name in ("tiny_decode", "decode_7b") else 0.0)
         log(f"[bench] oracle: {cpu}")
 
     rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "metric": METRIC, "value": round(main_run["value"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_run["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": T, "projections": n_proj,
+        "config": {"workload": wl.name, "tokens": wl.n_tokens, "projections": len(wl.projections),
                    "shape": [[p.d_in, p.d_out] for p in wl.projections],
-                   "active_adapters": len(active), "policy": args.policy,
+                   "active_adapters": main_run["active"], "policy": args.policy,
                    "instances_rotated": args.instances, "accumulate": "f32",
                    "page_elems": wl.page_elems, "pool_pages": wl.n_pages},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernels": kernels,
+        "kernels": main_run["kernels"],
         "kernel_timing": f"HIP events recorded by the launch at kernel start and end, on the launch "
-                         f"stream, for every kernel of 1 step in {ev}",
-        "step_kernel_us": round(kern_total_s * 1e6, 2),
-        "step_algorithmic_gbps": round(step_bytes / kern_total_s / 1e9, 1),
-        "fetch": {"bytes": fetch_bytes, "ms": round(float(np.median(fetch_ms)), 3),
-                  "gbps": round(fetch_bytes / (float(np.median(fetch_ms)) * 1e-3) / 1e9, 2)},
+                         f"stream, for every kernel of 1 step in {main_run['event_every']}; p10/p50/p90 "
+                         f"from {args.pct_steps} further steps with every launch timed",
+        "step_kernel_us": main_run["step_kernel_us"],
+        "step_algorithmic_gbps": main_run["step_algorithmic_gbps"],
+        "workspace_status": main_run["workspace_status"],
+        "copy_reference": copy_ref,
+        "fetch": fetch,
+        "prefill": prefill,
+        "device": dinfo,
     }
-    for inst, *_ in insts:
-        inst.close()
     print(json.dumps(rec), flush=True)
 
 

@@ -70,6 +70,8 @@ def load(path: str = LIB_PATH):
         "slora_pool_info": ([P, P, P, P, P], I),
         "slora_pool_alloc_kv": ([P, I, P], I),
         "slora_pool_free_kv": ([P, P, I], I),
+        "slora_pool_free": ([P, P, I], I),
+        "slora_pool_n_free": ([P, P], I),
         "slora_pool_alloc_adapter": ([P, I, I, I, P, P], I),
         "slora_pool_free_adapter": ([P, I], I),
         "slora_pool_page_table": ([P, I, I, P, _c_i64, P, P, P], I),
@@ -83,6 +85,8 @@ def load(path: str = LIB_PATH):
         "slora_timing_enable": ([I], I),
         "slora_workspace_status": ([P, P, P], I),
         "slora_timing_read": ([I, P, P], I),
+        "slora_timing_read_all": ([_c_i64, P, P, P], I),
+        "slora_set_wait_limit": ([I], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -139,6 +143,15 @@ class Pool:
     def free_kv(self, ids: np.ndarray):
         ids = np.ascontiguousarray(ids, np.int32)
         _check(self._lib.slora_pool_free_kv(self.handle, _p(ids), ids.size), "pool_free_kv")
+
+    def free(self, ids: np.ndarray):
+        ids = np.ascontiguousarray(ids, np.int32)
+        _check(self._lib.slora_pool_free(self.handle, _p(ids), ids.size), "pool_free")
+
+    def n_free(self) -> int:
+        n = _c_i64()
+        _check(self._lib.slora_pool_n_free(self.handle, ctypes.byref(n)), "pool_n_free")
+        return n.value
 
     def alloc_adapter(self, adapter_id: int, rank: int, d_in: Sequence[int], d_out: Sequence[int]):
         di = np.ascontiguousarray(d_in, np.int32)
@@ -256,8 +269,24 @@ def timing_read():
     return {k: (int(launches[i]), float(ms[i])) for i, k in enumerate(KERNELS)}
 
 
+def timing_read_all(cap: int = 1 << 16):
+    """Every timed launch since the last read: (kernel names [n], durations in ms [n]);
+    clears them."""
+    kernel = np.zeros(cap, np.int32)
+    ms = np.zeros(cap, np.float64)
+    n = _c_i64()
+    _check(load().slora_timing_read_all(cap, _p(kernel), _p(ms), ctypes.byref(n)), "timing_read_all")
+    return [KERNELS[k] for k in kernel[:n.value]], ms[:n.value].copy()
+
+
+def set_wait_limit(polls: int):
+    """Bound of the decode launches' wait for v, in polls (0 = the default, 2^20)."""
+    _check(load().slora_set_wait_limit(polls), "set_wait_limit")
+
+
 def workspace_status(ws: int, stream: int) -> int:
-    """0 if the last call on this workspace ran clean (synchronizes the stream)."""
+    """0 if every fused call on this workspace since the last status read ran clean;
+    1 if a wait gave up in one of them. Synchronizes the stream; clears the flag."""
     st = _c_i32()
     _check(load().slora_workspace_status(_vp(ws), _vp(stream), ctypes.byref(st)), "workspace_status")
     return st.value

@@ -26,12 +26,17 @@ namespace {
 // launch, ~3 us of GPU time per decode call). A group whose calls went to more than
 // one stream, or one of whose calls failed after taking its slot, is waited for with
 // a device synchronization when its slots come round again.
+//
+// Every slot (kSlotBytes of pinned memory) and every group event is created with the
+// ring, on a device's first compute call, so steady-state calls allocate nothing; a
+// slot grows (a new pinned buffer) only for a plan larger than it has held before.
 struct StagingSlot {
   void* host = nullptr;
   size_t cap = 0;
 };
 constexpr int kSlots = 16;
 constexpr int kGroup = 8;
+constexpr size_t kSlotBytes = size_t(1) << 20;
 struct SlotGroup {
   hipEvent_t ev = nullptr;
   bool pending = false;    // ev recorded and not yet waited for
@@ -42,8 +47,16 @@ struct Ring {
   StagingSlot slot[kSlots];
   SlotGroup grp[kSlots / kGroup];
   int next = 0;
+  bool ready = false;
+  // Fused decode launches wait across workgroups of one launch; two of them resident at
+  // once could each hold slots the other's shrinks need, so the library orders them:
+  // a fused launch on another stream than the previous one first waits for everything
+  // queued on that stream so far (one event, recorded only when the stream changes).
+  hipStream_t fused_stream = nullptr;
+  hipEvent_t fused_ev = nullptr;
 };
 std::mutex g_mu;  // guards the rings, the epoch map and the timing state
+int32_t g_spin_limit = kDefaultSpinLimit;  // decode expand waves' bounded wait
 std::map<int, Ring> g_rings;                 // per device
 std::map<const void*, uint32_t> g_ws_tag;  // last tag a fused call used, per workspace
 thread_local PlanScratch t_scratch;
@@ -54,11 +67,52 @@ struct SlotRef {
   void* host() const { return ring->slot[index].host; }
 };
 
+int grow_slot(StagingSlot& s, size_t n) {
+  if (s.host) (void)hipHostFree(s.host);
+  s.host = nullptr;
+  s.cap = 0;
+  size_t cap = kSlotBytes;
+  while (cap < n) cap <<= 1;
+  const hipError_t e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    s.host = nullptr;
+    return hip_fail(e, "staging: hipHostMalloc");
+  }
+  // touch every page now: the first write to each page of a new host mapping faults,
+  // which would otherwise cost the first planned call of each slot ~20 us
+  memset(s.host, 0, cap);
+  s.cap = cap;
+  return SLORA_OK;
+}
+
+// All slots and events of a device's ring, once.
+int ring_init(Ring& ring) {
+  if (ring.ready) return SLORA_OK;
+  for (StagingSlot& s : ring.slot)
+    if (!s.host) {
+      const int rc = grow_slot(s, kSlotBytes);
+      if (rc) return rc;
+    }
+  for (SlotGroup& g : ring.grp)
+    if (!g.ev) {
+      const hipError_t e = hipEventCreateWithFlags(&g.ev, hipEventDisableTiming);
+      if (e != hipSuccess) { g.ev = nullptr; return hip_fail(e, "staging: hipEventCreate"); }
+    }
+  if (!ring.fused_ev) {
+    const hipError_t e = hipEventCreateWithFlags(&ring.fused_ev, hipEventDisableTiming);
+    if (e != hipSuccess) { ring.fused_ev = nullptr; return hip_fail(e, "hipEventCreate"); }
+  }
+  ring.ready = true;
+  return SLORA_OK;
+}
+
 int acquire_slot(size_t n, hipStream_t stream, SlotRef* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   Ring& ring = g_rings[dev];
+  int rc = ring_init(ring);
+  if (rc) return rc;
   const int i = ring.next;
   SlotGroup& grp = ring.grp[i / kGroup];
   if (i % kGroup == 0) {  // the group comes round again: its previous calls must be done
@@ -72,10 +126,6 @@ int acquire_slot(size_t n, hipStream_t stream, SlotRef* out) {
       if (e != hipSuccess) return hip_fail(e, "staging: hipDeviceSynchronize");
       grp.unguarded = false;
     }
-    if (!grp.ev) {
-      e = hipEventCreateWithFlags(&grp.ev, hipEventDisableTiming);
-      if (e != hipSuccess) { grp.ev = nullptr; return hip_fail(e, "staging: hipEventCreate"); }
-    }
     grp.stream = stream;
   } else if (stream != grp.stream) {
     grp.unguarded = true;
@@ -83,23 +133,35 @@ int acquire_slot(size_t n, hipStream_t stream, SlotRef* out) {
   ring.next = (i + 1) % kSlots;
   StagingSlot& s = ring.slot[i];
   if (s.cap < n) {
-    if (s.host) (void)hipHostFree(s.host);
-    s.host = nullptr;
-    s.cap = 0;
-    size_t cap = 1 << 16;
-    while (cap < n) cap <<= 1;
-    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
-    if (e != hipSuccess) {
-      s.host = nullptr;
+    rc = grow_slot(s, n);
+    if (rc) {
       grp.unguarded = true;
-      return hip_fail(e, "staging: hipHostMalloc");
+      return rc;
     }
-    s.cap = cap;
   }
   out->ring = &ring;
   out->index = i;
   return SLORA_OK;
 }
+
+// Orders work about to go to `s` after everything queued so far on `*last` (the stream
+// of the previous launch of its kind on this device) when that is another stream.
+int order_after(hipStream_t* last, hipEvent_t ev, hipStream_t s) {
+  if (*last != nullptr && *last != s) {
+    hipError_t e = hipEventRecord(ev, *last);
+    if (e == hipSuccess) {
+      e = hipStreamWaitEvent(s, ev, 0);
+      if (e != hipSuccess) return hip_fail(e, "launch ordering: hipStreamWaitEvent");
+    } else {  // that stream was destroyed since: wait for all work on the device instead
+      (void)hipGetLastError();
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "launch ordering: hipDeviceSynchronize");
+    }
+  }
+  *last = s;
+  return SLORA_OK;
+}
+int order_fused(Ring& ring, hipStream_t s) { return order_after(&ring.fused_stream, ring.fused_ev, s); }
 
 // After a call's launches (ok) or a failure after acquire_slot (!ok): the group's last
 // call records the group's event.
@@ -129,6 +191,15 @@ struct TimedLaunch {
 bool g_timing_on = false;
 std::vector<TimedLaunch> g_timed;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_spare_events;
+constexpr size_t kTimingEvents = 512;  // event pairs created when timing is enabled
+
+hipError_t new_event_pair(std::pair<hipEvent_t, hipEvent_t>* ev) {
+  hipError_t e = hipEventCreate(&ev->first);
+  if (e != hipSuccess) return e;
+  e = hipEventCreate(&ev->second);
+  if (e != hipSuccess) (void)hipEventDestroy(ev->first);
+  return e;
+}
 
 template <typename F>
 hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
@@ -137,11 +208,9 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
   if (!g_spare_events.empty()) {
     ev = g_spare_events.back();
     g_spare_events.pop_back();
-  } else {
-    hipError_t e = hipEventCreate(&ev.first);
+  } else {  // more timed launches than were prepared for
+    const hipError_t e = new_event_pair(&ev);
     if (e != hipSuccess) return e;
-    e = hipEventCreate(&ev.second);
-    if (e != hipSuccess) { (void)hipEventDestroy(ev.first); return e; }
   }
   LaunchEvents le;
   le.start = ev.first;
@@ -161,7 +230,7 @@ bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 
 int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv, const void* x,
                 float* v_out, const float* v_in, void* y, void* ws, int64_t ws_bytes,
-                const WsLayout& lay, hipStream_t s, int mode);
+                const WsLayout& lay, hipStream_t s, int mode, Ring* ring);
 
 int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out,
         const float* v_in, void* y, void* ws, int64_t ws_bytes, void* stream, int mode) {
@@ -190,7 +259,7 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
   int rc = acquire_slot((size_t)bytes, s, &slot);
   if (rc) return rc;
   plan_write(L, R, &t_scratch, slot.host(), &pv);  // kernels read this host buffer directly
-  rc = launch_plan(L, R, pv, x, v_out, v_in, y, ws, ws_bytes, lay, s, mode);
+  rc = launch_plan(L, R, pv, x, v_out, v_in, y, ws, ws_bytes, lay, s, mode, slot.ring);
   const int rc2 = release_slot(slot, s, rc == SLORA_OK);
   return rc ? rc : rc2;
 }
@@ -198,7 +267,7 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
 // The launches of one planned call (the work list is in a pinned staging slot).
 int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv, const void* x,
                 float* v_out, const float* v_in, void* y, void* ws, int64_t ws_bytes,
-                const WsLayout& lay, hipStream_t s, int mode) {
+                const WsLayout& lay, hipStream_t s, int mode, Ring* ring) {
   uint8_t* wsb = (uint8_t*)ws;
   Geom g;
   g.pool = (const uint16_t*)L->pool;
@@ -217,15 +286,18 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
   hipError_t e = hipSuccess;
   uint32_t tag = 0;
   if (mode == kApply && pv.n_mb) {
-    // A fresh tag per fused call on this workspace; before a tag could repeat,
-    // the whole workspace is cleared so no stale word can carry it.
+    // A fresh tag per fused call on this workspace; before a tag could repeat, the
+    // workspace past its header is cleared so no stale word can carry it (the header
+    // keeps any give-up until slora_workspace_status reads it).
     uint32_t& last = g_ws_tag[ws];
     if (last == 0xFFFFFFFFu) {
-      e = launch_zero(ws, ws_bytes & ~(int64_t)255, s);
+      e = launch_zero(wsb + kHeaderBytes, (ws_bytes & ~(int64_t)255) - kHeaderBytes, s);
       if (e != hipSuccess) return hip_fail(e, "workspace clear");
       last = 0;
     }
     tag = ++last;
+    const int rc = order_fused(*ring, s);
+    if (rc) return rc;
   }
   if (pv.n_sg) {
     // apply: k-range partials in the workspace; shrink / expand only: one range,
@@ -281,17 +353,18 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
     if (mode == kApply) {
       e = timed_launch(SLORA_K_MBGMV_FUSED, s, [&](const LaunchEvents& le) {
         return launch_mbgmv(g, pv.mb, pv.n_mb, pv.n_mb_shrink > 0, has_expand, pv.mb_max_tok, x,
-                            v, y, tag, err, s, le);
+                            v, y, tag, err, g_spin_limit, s, le);
       });
     } else if (mode == kShrink) {
       e = timed_launch(SLORA_K_MBGMV_SHRINK, s, [&](const LaunchEvents& le) {
         return launch_mbgmv(g, pv.mb, pv.n_mb_shrink, true, false, pv.mb_max_tok, x, v, nullptr, 0,
-                            err, s, le);
+                            err, g_spin_limit, s, le);
       });
     } else {
       e = timed_launch(SLORA_K_MBGMV_EXPAND, s, [&](const LaunchEvents& le) {
         return launch_mbgmv(g, pv.mb + pv.n_mb_shrink, pv.n_mb - pv.n_mb_shrink, false, true,
-                            pv.mb_max_tok, nullptr, const_cast<float*>(vr), y, 0, err, s, le);
+                            pv.mb_max_tok, nullptr, const_cast<float*>(vr), y, 0, err, g_spin_limit,
+                            s, le);
       });
     }
     if (e != hipSuccess) return hip_fail(e, "mbgmv launch");
@@ -306,7 +379,22 @@ extern "C" {
 static int impl_slora_timing_enable(int32_t on) {
   clear_error();
   std::lock_guard<std::mutex> lk(g_mu);
+  // the event pairs timed launches take are created here, not inside compute calls
+  while (on && g_spare_events.size() + g_timed.size() < kTimingEvents) {
+    std::pair<hipEvent_t, hipEvent_t> ev;
+    const hipError_t e = new_event_pair(&ev);
+    if (e != hipSuccess) return hip_fail(e, "timing_enable: hipEventCreate");
+    g_spare_events.push_back(ev);
+  }
   g_timing_on = on != 0;
+  return SLORA_OK;
+}
+
+static int impl_slora_set_wait_limit(int32_t polls) {
+  clear_error();
+  if (polls < 0) return fail(SLORA_E_INVALID, "set_wait_limit: polls %d < 0", polls);
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_spin_limit = polls == 0 ? kDefaultSpinLimit : polls;
   return SLORA_OK;
 }
 
@@ -332,6 +420,31 @@ static int impl_slora_timing_read(int32_t n_kernels, int64_t* launches, double* 
   return rc;
 }
 
+static int impl_slora_timing_read_all(int64_t cap, int32_t* kernel, double* ms, int64_t* n) {
+  clear_error();
+  if (!n || cap < 0 || (cap > 0 && (!kernel || !ms)))
+    return fail(SLORA_E_INVALID, "timing_read_all: bad arguments");
+  std::lock_guard<std::mutex> lk(g_mu);
+  *n = (int64_t)g_timed.size();
+  if (*n > cap)
+    return fail(SLORA_E_INVALID, "timing_read_all: %lld launches recorded, room for %lld",
+                (long long)*n, (long long)cap);
+  int rc = SLORA_OK;
+  int64_t i = 0;
+  for (auto& t : g_timed) {
+    hipError_t e = hipEventSynchronize(t.stop);
+    float f = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&f, t.start, t.stop);
+    if (e != hipSuccess && rc == SLORA_OK) rc = hip_fail(e, "timing_read_all");
+    kernel[i] = t.kernel;
+    ms[i] = f;
+    ++i;
+    g_spare_events.push_back({t.start, t.stop});
+  }
+  g_timed.clear();
+  return rc;
+}
+
 static int impl_slora_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes) {
   clear_error();
   if (!lora || !routing || !bytes) return fail(SLORA_E_INVALID, "workspace_size: NULL argument");
@@ -339,16 +452,19 @@ static int impl_slora_workspace_size(const slora_lora* lora, const slora_routing
   return SLORA_OK;
 }
 
-static int impl_slora_workspace_status(const void* ws, void* stream, int32_t* status) {
+static int impl_slora_workspace_status(void* ws, void* stream, int32_t* status) {
   clear_error();
   if (!ws || !status) return fail(SLORA_E_INVALID, "workspace_status: NULL argument");
   unsigned long long flag = 0;
-  hipError_t e = hipMemcpyAsync(&flag, ws, sizeof flag, hipMemcpyDeviceToHost, (hipStream_t)stream);
-  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&flag, ws, sizeof flag, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && flag != 0) {  // report once: the word is cleared for the next calls
+    e = hipMemsetAsync(ws, 0, sizeof flag, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+  }
   if (e != hipSuccess) return hip_fail(e, "workspace_status");
-  std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_ws_tag.find(ws);
-  *status = (it != g_ws_tag.end() && it->second != 0 && flag == it->second) ? 1 : 0;
+  *status = flag != 0 ? 1 : 0;
   return SLORA_OK;
 }
 
@@ -430,8 +546,16 @@ int slora_workspace_size(const slora_lora* lora, const slora_routing* routing, i
   return slora::guarded(__func__, [&] { return impl_slora_workspace_size(lora, routing, bytes); });
 }
 
-int slora_workspace_status(const void* ws, void* stream, int32_t* status) {
+int slora_workspace_status(void* ws, void* stream, int32_t* status) {
   return slora::guarded(__func__, [&] { return impl_slora_workspace_status(ws, stream, status); });
+}
+
+int slora_set_wait_limit(int32_t polls) {
+  return slora::guarded(__func__, [&] { return impl_slora_set_wait_limit(polls); });
+}
+
+int slora_timing_read_all(int64_t cap, int32_t* kernel, double* ms, int64_t* n) {
+  return slora::guarded(__func__, [&] { return impl_slora_timing_read_all(cap, kernel, ms, n); });
 }
 
 int slora_shrink(const slora_lora* lora, const slora_routing* routing, const void* x, float* v,

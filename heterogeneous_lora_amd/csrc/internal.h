@@ -29,7 +29,6 @@ constexpr int kAutoSgmvTok = 4;     // AUTO: an adapter's per-token ids go to SG
 constexpr int kAutoSgmvBatch = 256; // AUTO: ... when at least this many such tokens (or segments run)
 constexpr int kAutoSgmvShare = 4;   // ... and they are at least 1 / (1 + this) of the per-token ids
 constexpr int kAutoMbgmvMin = 128;  // AUTO: fewer per-token ids left for MBGMV join SGMV when it runs
-constexpr int kXcds = 8;            // XCDs (dies, each with its own L2) workgroups are dealt to in turn
 constexpr int kSgMaxSplit = 8;      // SGMV shrink: most k-ranges d_in is cut into
 
 // k-ranges the SGMV shrink may cut d_in into (each at least 256 long).
@@ -121,7 +120,8 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
                 PlanView* out);
 
 // Workspace (device, caller-owned, zero-filled once at allocation):
-//   [0, 256): header: uint64 tag of the last call whose wait gave up
+//   [0, 256): header: uint64, nonzero once a fused call's wait gave up (sticky until
+//             slora_workspace_status reads and clears it)
 //   v_off: MBGMV v as uint64 words [n_tokens x r_max]: (tag << 32) | fp32 bits
 //   sg_off: SGMV partial v, fp32 [sg_max_split(d_in)][n_tokens x sg_v_stride(r_max)]
 constexpr int64_t kHeaderBytes = 256;
@@ -139,9 +139,11 @@ struct LaunchEvents {
 // One launch over items (role per item; `shrinks` / `expands` say which roles
 // occur). tag != 0 makes it a fused apply: v is the workspace's tagged words,
 // shrink items write them and expand items poll them. tag == 0: v is plain fp32.
+// spin_limit: polls an expand wave makes for its v before it gives up (fused only).
+constexpr int32_t kDefaultSpinLimit = 1 << 20;
 hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
                         bool expands, int32_t max_tok, const void* x, void* v, void* y,
-                        uint32_t tag, unsigned long long* err, hipStream_t s,
+                        uint32_t tag, unsigned long long* err, int32_t spin_limit, hipStream_t s,
                         const LaunchEvents& ev = LaunchEvents());
 // Zero `bytes` (a multiple of 16) of device memory with a kernel.
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s);

@@ -36,8 +36,8 @@
 // Forward progress: workgroups are dispatched in index order on each XCD and a
 // shrink workgroup never waits, so every shrink an expand wave depends on has
 // been dispatched before it and finishes. Every wait is bounded anyway: past
-// kSpinLimit polls the wave records the tag in the error word and goes on, so no
-// wave can spin forever.
+// `spin_limit` polls (set by the host, 2^20 by default) the wave records the tag in
+// the error word and goes on, so no wave can spin forever.
 //
 // Every page load issues unconditionally: rows past the rank, invalid page ids and
 // lanes past the end of a row are pointed at 16-byte fill vectors (zero or NaN)
@@ -55,7 +55,6 @@ static_assert(kWaves * kRowsPerWave == kMbShrinkRows, "shrink row block");
 constexpr int kBatchVecs = 512;  // 16-byte vectors of a row per shrink batch (4096 elements)
 constexpr int kSlices = kBatchVecs / 64;
 constexpr int kKU = kMbRowsPerWave;
-constexpr int kSpinLimit = 1 << 20;
 constexpr int kRedBytes = (kWaves - 1) * kMbExpandTok * 8 * 64 * 4;  // expand partial sums
 
 __device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
@@ -158,7 +157,8 @@ __device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
 template <int DT, bool kUniformChunk, int NT, bool kTag>
 __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
                                             const void* __restrict__ v, uint16_t* __restrict__ y,
-                                            uint32_t tag, unsigned long long* err, float* red) {
+                                            uint32_t tag, unsigned long long* err, int32_t spin_limit,
+                                            float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = it.rank, n = it.n_tok(), split = it.split();
   const int slices = kWaves / split, slice = wave / split, rp = wave % split;
@@ -217,7 +217,7 @@ __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
         ready = ready && (!(t < n && lane < nk) || (uint32_t)(w[t] >> 32) == tag);
       }
       if (__all(ready)) break;
-      if (spins >= kSpinLimit) {
+      if (spins >= spin_limit) {
         if (lane == 0) __hip_atomic_store(err, (unsigned long long)tag, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -302,7 +302,7 @@ __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
 template <int DT, bool kUniformChunk, bool kTag>
 __global__ __launch_bounds__(64 * kWaves) void mbgmv_kernel(
     Geom g, const MbItem* __restrict__ items, const uint16_t* __restrict__ x, void* v,
-    uint16_t* __restrict__ y, uint32_t tag, unsigned long long* err) {
+    uint16_t* __restrict__ y, uint32_t tag, unsigned long long* err, int32_t spin_limit) {
   extern __shared__ uint4 lds[];  // shrink: [G][kBatchVecs] of x; expand: partial sums
   const MbItem it = items[blockIdx.x];
   if (it.role() == 0) {
@@ -313,24 +313,25 @@ __global__ __launch_bounds__(64 * kWaves) void mbgmv_kernel(
     else shrink_body<DT, kUniformChunk, 4, kTag>(g, it, x, v, tag, lds);
   } else {
     float* red = reinterpret_cast<float*>(lds);
-    if (it.n_tok() <= 1) expand_body<DT, kUniformChunk, 1, kTag>(g, it, v, y, tag, err, red);
-    else expand_body<DT, kUniformChunk, 2, kTag>(g, it, v, y, tag, err, red);
+    if (it.n_tok() <= 1) expand_body<DT, kUniformChunk, 1, kTag>(g, it, v, y, tag, err, spin_limit, red);
+    else expand_body<DT, kUniformChunk, 2, kTag>(g, it, v, y, tag, err, spin_limit, red);
   }
 }
 
 template <int DT, bool kTag>
 hipError_t launch_dt(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
                      bool expands, int32_t g_max, const void* x, void* v, void* y, uint32_t tag,
-                     unsigned long long* err, hipStream_t s, const LaunchEvents& ev) {
+                     unsigned long long* err, int32_t spin_limit, hipStream_t s,
+                     const LaunchEvents& ev) {
   const dim3 grid((unsigned)n_items), block(64 * kWaves);
   size_t lds = shrinks ? (size_t)g_max * kBatchVecs * sizeof(uint4) : 0;
   if (expands) lds = lds > (size_t)kRedBytes ? lds : (size_t)kRedBytes;
   if (g.P % 512 == 0)
     hipExtLaunchKernelGGL((mbgmv_kernel<DT, true, kTag>), grid, block, lds, s, ev.start, ev.stop, 0,
-                          g, items, (const uint16_t*)x, v, (uint16_t*)y, tag, err);
+                          g, items, (const uint16_t*)x, v, (uint16_t*)y, tag, err, spin_limit);
   else
     hipExtLaunchKernelGGL((mbgmv_kernel<DT, false, kTag>), grid, block, lds, s, ev.start, ev.stop, 0,
-                          g, items, (const uint16_t*)x, v, (uint16_t*)y, tag, err);
+                          g, items, (const uint16_t*)x, v, (uint16_t*)y, tag, err, spin_limit);
   return hipGetLastError();
 }
 
@@ -343,17 +344,18 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n) {
 
 hipError_t launch_mbgmv(const Geom& g, const MbItem* items, int32_t n_items, bool shrinks,
                         bool expands, int32_t max_tok, const void* x, void* v, void* y,
-                        uint32_t tag, unsigned long long* err, hipStream_t s, const LaunchEvents& ev) {
+                        uint32_t tag, unsigned long long* err, int32_t spin_limit, hipStream_t s,
+                        const LaunchEvents& ev) {
   if (n_items <= 0) return hipSuccess;
   if (max_tok < 1 || max_tok > kMbGroup) return hipErrorInvalidValue;
   const int g_max = max_tok <= 1 ? 1 : max_tok <= 2 ? 2 : 4;
   if (tag)
     return g.dtype == SLORA_F16
-               ? launch_dt<SLORA_F16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, s, ev)
-               : launch_dt<SLORA_BF16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, s, ev);
+               ? launch_dt<SLORA_F16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, spin_limit, s, ev)
+               : launch_dt<SLORA_BF16, true>(g, items, n_items, shrinks, expands, g_max, x, v, y, tag, err, spin_limit, s, ev);
   return g.dtype == SLORA_F16
-             ? launch_dt<SLORA_F16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, s, ev)
-             : launch_dt<SLORA_BF16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, s, ev);
+             ? launch_dt<SLORA_F16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, spin_limit, s, ev)
+             : launch_dt<SLORA_BF16, false>(g, items, n_items, shrinks, expands, g_max, x, v, y, 0, err, spin_limit, s, ev);
 }
 
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s) {

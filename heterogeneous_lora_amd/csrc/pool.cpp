@@ -415,6 +415,17 @@ int slora_pool_free_kv(slora_pool* pool, const int32_t* page_ids, int32_t n) {
   return slora::guarded(__func__, [&] { return impl_slora_pool_free_kv(pool, page_ids, n); });
 }
 
+int slora_pool_free(slora_pool* pool, const int32_t* page_ids, int32_t n) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_free_kv(pool, page_ids, n); });
+}
+
+int slora_pool_n_free(const slora_pool* pool, int64_t* n_free) {
+  return slora::guarded(__func__, [&] {
+    if (!n_free) return fail(SLORA_E_INVALID, "pool_n_free: n_free is NULL");
+    return impl_slora_pool_info(pool, nullptr, n_free, nullptr, nullptr);
+  });
+}
+
 int slora_pool_alloc_adapter(slora_pool* pool, int32_t adapter_id, int32_t rank, int32_t n_proj,
                              const int32_t* d_in, const int32_t* d_out) {
   return slora::guarded(__func__, [&] { return impl_slora_pool_alloc_adapter(pool, adapter_id, rank, n_proj, d_in, d_out); });

@@ -108,8 +108,16 @@ int slora_pool_info(const slora_pool* pool, int64_t* n_pages, int64_t* n_free,
  * out_page_ids[n]. SLORA_E_POOL_FULL (nothing taken) if fewer than n are free. */
 int slora_pool_alloc_kv(slora_pool* pool, int32_t n, int32_t* out_page_ids);
 
-/* Return KV pages to the free list. Every id must be a KV page of this pool. */
+/* Return KV pages to the free list. Every id must be a KV page of this pool;
+ * all-or-nothing (SLORA_E_INVALID and nothing freed on a bad or repeated id). */
 int slora_pool_free_kv(slora_pool* pool, const int32_t* page_ids, int32_t n);
+
+/* The same as slora_pool_free_kv (the name the scope of this library gives the call
+ * that returns pages to the shared free list). */
+int slora_pool_free(slora_pool* pool, const int32_t* page_ids, int32_t n);
+
+/* Free pages of the pool in *n_free (slora_pool_info's n_free alone). */
+int slora_pool_n_free(const slora_pool* pool, int64_t* n_free);
 
 /* Reserve pages for adapter `adapter_id` (>= 0): rank r >= 0 (shared by its
  * projections) and n_proj projections with shapes d_in[p] x d_out[p] (multiples
@@ -200,15 +208,32 @@ int slora_expand(const slora_lora* lora, const slora_routing* routing, const flo
  * Decode tokens run in one launch: shrink workgroups publish v per group and the
  * group's expand workgroups wait for it (a bounded wait; see
  * slora_workspace_status). The work list is read by the kernels from a pinned
- * host staging ring owned by the library. */
+ * host staging ring owned by the library.
+ * Two such decode launches resident on one device at once could each hold the
+ * compute slots the other's shrink workgroups need, so the library orders them: a
+ * call whose decode launch goes to another stream than the previous decode launch
+ * on the device first makes its stream wait for the work queued on that previous
+ * stream (an event recorded there; if that stream no longer exists, a device
+ * synchronization). Decode launches from other processes sharing the device are
+ * not ordered. */
 int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
                 void* ws, int64_t ws_bytes, void* stream);
 
-/* Status of the last slora_apply that used workspace ws, once the work on
- * `stream` has finished (this call synchronizes the stream): 0 = clean; 1 = a
- * decode workgroup gave up waiting for v that another workgroup of the same
- * launch should have published (that call's results are not valid). */
-int slora_workspace_status(const void* ws, void* stream, int32_t* status);
+/* Status of the slora_apply calls that used workspace ws since the previous status
+ * read, once the work on `stream` has finished (this call synchronizes the stream):
+ * 0 = clean; 1 = in at least one of them a decode workgroup gave up waiting for v
+ * that another workgroup of the same launch should have published (that call's
+ * results are not valid). The give-up is sticky in the workspace header until this
+ * call reads it, and reading clears it. */
+int slora_workspace_status(void* ws, void* stream, int32_t* status);
+
+/* Bound of the wait in decode launches: an expand wave polls for its v at most `polls`
+ * times before it gives up (see slora_workspace_status). polls = 0 restores the default
+ * (2^20 polls, far beyond any wait a valid launch has). Applies to launches made after
+ * the call, on every device. Tests of the give-up path set a small bound (1 poll: waves
+ * that find v not yet published give up at once, so the launch ends with invalid
+ * results and a set status instead of waiting). */
+int slora_set_wait_limit(int32_t polls);
 
 /* Kernel timing for benchmarks. While enabled (on != 0), every kernel a compute
  * call launches carries two HIP events that the launch itself records on the call's
@@ -230,6 +255,13 @@ int slora_timing_enable(int32_t on);
  * launches and their summed duration in milliseconds (arrays of n_kernels entries,
  * n_kernels <= SLORA_K_COUNT), and clears the counters. */
 int slora_timing_read(int32_t n_kernels, int64_t* launches, double* total_ms);
+
+/* Every timed launch since the last read, in launch order: kernel[i] its kernel id,
+ * ms[i] its duration (arrays of cap entries); *n gets the count (SLORA_E_INVALID,
+ * nothing cleared, if it exceeds cap). Waits for the events, then clears them. The
+ * event pairs are created by slora_timing_enable (512 of them), so timed compute
+ * calls create none unless more launches are timed before a read. */
+int slora_timing_read_all(int64_t cap, int32_t* kernel, double* ms, int64_t* n);
 
 /* Work lists a call with these arguments would run, for inspection and tests
  * (host only; validates exactly like slora_apply, launches nothing). Groups come

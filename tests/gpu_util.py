@@ -32,6 +32,30 @@ def check_close(y_gpu_bits, y_ref, dtype, what=""):
     return err / scale
 
 
+def margin_line(what, rel):
+    """One greppable line per parity check: max|y - y_ref| / max(1, ||y_ref||_inf) and the
+    tolerance, so the margins of every workload and routing policy are on record."""
+    say(f"[margin] {what}: max_err/scale={rel:.3e} tol={TOL:.0e} ratio={rel / TOL:.3f}")
+
+
+def full_rows_rel(y_gpu_bits, wl, proj, dtype, what, chunk=2048, n_threads=16):
+    """Every output row against the oracle, in chunks of rows to bound host memory.
+    The tolerance is the global one: max over all rows of |y - y_ref| against
+    TOL * max(1, max over all rows of |y_ref|)."""
+    T = wl.n_tokens
+    err, ref_max = 0.0, 0.0
+    for c0 in range(0, T, chunk):
+        ev = np.arange(c0, min(T, c0 + chunk), dtype=np.int64)
+        ref, _ = oracle.reference(wl, proj, ev, n_threads=n_threads)
+        y = decode(y_gpu_bits[ev], dtype)
+        assert np.all(np.isfinite(y)), f"{what}: non-finite GPU output in rows {c0}.."
+        err = max(err, float(np.max(np.abs(y - ref))))
+        ref_max = max(ref_max, float(np.max(np.abs(ref))))
+    scale = max(1.0, ref_max)
+    assert err <= TOL * scale, f"{what}: max err {err:.3e} > {TOL} * {scale:.3f}"
+    return err / scale
+
+
 def sample_tokens(wl, n, seed=0):
     """Evaluation rows: ends of every segment (ragged tails), both ends of the batch, random rest."""
     T = wl.n_tokens

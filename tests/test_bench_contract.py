@@ -40,5 +40,17 @@ def test_bench_prints_one_json_line():
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert 0 < r["achieved"] < r["peak"] and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    assert r["copy_gbps"] > 0 and r["frac_of_copy"] > 0
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["unit"] == "tokens/s"
+    assert c["single_thread"]["cores"] == 1 and c["single_thread"]["value"] > 0
+    assert d["workspace_status"] == "clean"
+    k = d["kernels"][r["kernel"]]
+    assert k["p10_us"] <= k["p50_us"] <= k["p90_us"] and k["pct_launches"] >= 8
+    assert d["fetch"]["h2d_copy_engine_gbps"] > 0
+    assert d["device"]["compute_units"] > 0
+    pf = d["prefill"]
+    assert pf["workload"] == "prefill_sgmv" and pf["value"] > 0 and pf["workspace_status"] == "clean"
+    for kern in ("sgmv_shrink", "sgmv_expand"):
+        pr = pf["roofline"][kern]
+        assert pr["unit"] == "GB/s" and 0 < pr["frac"] < 1 and 0 < pr["mfma_frac"] < 1

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import (TOL, CodedWorkload, check_close, coded, oracle_ref, sample_tokens, say)
+from gpu_util import (TOL, CodedWorkload, check_close, coded, full_rows_rel, margin_line, oracle_ref,
+                      sample_tokens, say)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -75,7 +76,7 @@ def test_small_parity(rt, kw, policy):
     say(f"[gpu] small parity {kw} policy={policy}")
     y, inst = _run(rt, wl, policy=policy)
     ref, _ = oracle_ref(wl, 0)
-    check_close(y, ref, wl.dtype, f"small {kw}")
+    margin_line(f"small s{kw['seed']} policy={POLICY_IDS[policy]}", check_close(y, ref, wl.dtype, f"small {kw}"))
     inst.close()
 
 
@@ -143,7 +144,7 @@ def test_tiny_decode_parity(rt, policy):
     say(f"[gpu] tiny_decode parity policy={policy}")
     y, inst = _run(rt, wl, policy=policy)
     ref, _ = oracle_ref(wl, 0)
-    check_close(y, ref, wl.dtype, "tiny_decode")
+    margin_line(f"tiny_decode policy={POLICY_IDS[policy]} all rows", check_close(y, ref, wl.dtype, "tiny_decode"))
     inst.close()
 
 
@@ -162,7 +163,7 @@ def test_decode7b_parity(rt, decode7b):
     y, _ = _run(rt, wl, inst=inst)
     ref, _ = oracle_ref(wl, 0)
     rel = check_close(y, ref, wl.dtype, "decode_7b")
-    say(f"[gpu] decode_7b max err / scale = {rel:.2e} (tol {TOL})")
+    margin_line("decode_7b policy=auto all rows", rel)
 
 
 def test_decode7b_sgmv_parity(rt, decode7b):
@@ -171,7 +172,7 @@ def test_decode7b_sgmv_parity(rt, decode7b):
     say("[gpu] decode_7b parity through SGMV")
     y, _ = _run(rt, wl, inst=inst, policy=2)
     ref, _ = oracle_ref(wl, 0)
-    check_close(y, ref, wl.dtype, "decode_7b sgmv")
+    margin_line("decode_7b policy=sgmv all rows", check_close(y, ref, wl.dtype, "decode_7b sgmv"))
 
 
 @pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
@@ -430,18 +431,144 @@ LARGE = [("mixed_13b", 1), ("mlp_asym", 1), ("prefill_sgmv", 0), ("mixed_13b", 0
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,policy", LARGE, ids=[f"{n}-{POLICY_IDS[p]}" for n, p in LARGE])
 def test_large_sampled(rt, name, policy):
-    """Full-size workloads, checked on sampled rows (segment ends, batch ends, random)."""
+    """Full-size workloads, every projection, checked on sampled rows (segment ends, batch
+    ends, random); the projections checked on every row are in test_large_full_rows."""
     wl = workloads.make(name)
     say(f"[gpu] {name} policy={policy}, building instance")
     inst = rt.PagedLoRA(wl)
     ev = sample_tokens(wl, 48)
     for proj in range(len(wl.projections)):
-        say(f"[gpu] {name} proj {wl.projections[proj].name} policy={policy}")
+        pname = wl.projections[proj].name
+        say(f"[gpu] {name} proj {pname} policy={policy}")
         y, _ = _run(rt, wl, proj=proj, policy=policy, inst=inst)
         ref, _ = oracle_ref(wl, proj, ev)
-        check_close(y[ev], ref, wl.dtype, f"{name}/{proj}")
+        rel = check_close(y[ev], ref, wl.dtype, f"{name}/{proj}")
+        margin_line(f"{name} proj={pname} policy={POLICY_IDS[policy]} {ev.size} sampled rows", rel)
         ids = np.concatenate([np.repeat(wl.seg_adapter, np.diff(wl.seg_offsets)), wl.token_adapter])
         idle = ids < 0
         if idle.any():
             assert np.array_equal(y[idle], wl.y0(proj)[idle])
     inst.close()
+
+
+# (workload, projections checked on every output row, routing policy)
+FULL = [("prefill_sgmv", ("q",), 0), ("mixed_13b", ("q",), 0), ("mlp_asym", ("up", "down"), 0)]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,projs,policy", FULL, ids=[f"{n}-{'+'.join(p)}" for n, p, _ in FULL])
+def test_large_full_rows(rt, name, projs, policy):
+    """Full-size workloads against the oracle on every output row of the named
+    projections (the launch configuration the benchmark times): the prefill batch
+    through SGMV (v rounded once to bf16 before the MFMA expand), the mixed batch
+    through both families, the MLP shapes at 4096 -> 11008 and 11008 -> 4096."""
+    wl = workloads.make(name)
+    say(f"[gpu] {name} full rows, building instance")
+    inst = rt.PagedLoRA(wl)
+    for pname in projs:
+        proj, _ = wl.proj(pname)
+        say(f"[gpu] {name} proj {pname} policy={POLICY_IDS[policy]}: GPU apply, then oracle on all "
+            f"{wl.n_tokens} rows")
+        y, _ = _run(rt, wl, proj=proj, policy=policy, inst=inst)
+        rel = full_rows_rel(y, wl, proj, wl.dtype, f"{name}/{pname}")
+        margin_line(f"{name} proj={pname} policy={POLICY_IDS[policy]} all {wl.n_tokens} rows", rel)
+    inst.close()
+
+
+@pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
+def test_expand_probe_codes_bit_exact(rt, policy):
+    """Expand probe: v = e_k (token t reads rank row k_t alone), B rows hold integer codes,
+    y0 = 0 and the scale a power of two, so y[t, :] = s * B[k_t, :] exactly: every B page
+    gather (three chunks per row, the last one ragged) and every token's routing read back
+    bit for bit, through slora_expand, for both element types."""
+    for dt in ("f16", "bf16"):
+        base_wl = workloads.random_small(207, dtype=dt, d_in=520, d_out=1040, page_elems=512,
+                                         n_tokens=26, n_segments=0, rank_choices=(4, 8, 16),
+                                         p_none=0.0, n_adapters=5)
+        wl = coded(base_wl)
+        say(f"[gpu] expand probe {dt} policy={POLICY_IDS[policy]}")
+        inst = rt.PagedLoRA(wl)
+        p = wl.projections[0]
+        call = inst.call(0, policy)
+        ids = wl.token_adapter
+        ks = np.array([np.random.default_rng(9 + t).integers(int(wl.ranks[a])) for t, a in enumerate(ids)])
+        v = np.zeros((wl.n_tokens, inst.r_max), np.float32)
+        v[np.arange(wl.n_tokens), ks] = 1.0
+        y = torch.zeros(wl.n_tokens, p.d_out, dtype=torch.int16, device="cuda")  # y0 = +0
+        ws = inst.workspace(call)
+        inst.expand(call, torch.from_numpy(v).cuda(), y, ws)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().view(np.uint16)
+        for t in range(wl.n_tokens):
+            a = int(ids[t])
+            s = float(wl.scales[a])
+            assert s in (1.0, 2.0, 4.0)
+            codes = np.array([CodedWorkload.code(a, 0, int(ks[t]), n, 1) for n in range(p.d_out)],
+                             np.float32)
+            want = workloads.to_bits(codes * np.float32(s), dt)
+            assert np.array_equal(got[t], want), (dt, t, a, int(ks[t]))
+        inst.close()
+
+
+def test_wait_giveup_is_sticky_and_cleared(rt, decode7b):
+    """The decode launch's bounded wait, forced short from the host (every kernel still
+    ends normally): a give-up in any of several calls is reported by the next status
+    read, which clears it; with the default bound the same calls run clean and match
+    the oracle."""
+    from heterogeneous_lora_amd import _lib
+    wl, inst = decode7b
+    say("[gpu] decode_7b with a 1-poll wait bound: give-ups reported, then cleared")
+    call = inst.call(0)
+    x, y0 = inst.inputs(0)
+    ws = inst.workspace(call)
+    stream = torch.cuda.current_stream().cuda_stream
+    try:
+        _lib.set_wait_limit(1)
+        for _ in range(6):
+            y = y0.clone()
+            inst.apply(call, x, y, ws)
+    finally:
+        _lib.set_wait_limit(0)
+    assert _lib.workspace_status(ws.data_ptr(), stream) == 1
+    assert _lib.workspace_status(ws.data_ptr(), stream) == 0  # read once, then clear
+    say("[gpu] decode_7b with the default wait bound after the give-ups")
+    y = y0.clone()
+    inst.apply(call, x, y, ws)
+    assert _lib.workspace_status(ws.data_ptr(), stream) == 0
+    ref, _ = oracle_ref(wl, 0)
+    check_close(y.cpu().numpy().view(np.uint16), ref, wl.dtype, "decode_7b after give-ups")
+
+
+def test_two_stream_decode_applies(rt, decode7b):
+    """Decode applies of the 7B batch on two workspaces and two streams, issued
+    alternately with the host far ahead of the GPU: the library orders the fused
+    launches across the streams, every output matches the oracle and both workspaces
+    report a clean status."""
+    wl, inst = decode7b
+    say("[gpu] decode_7b applies alternating over two streams")
+    ref, _ = oracle_ref(wl, 0)
+    x, y0 = inst.inputs(0)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    calls = [inst.call(0), inst.call(0)]
+    wss = [inst.workspace(c) for c in calls]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(20_000_000)  # bounded spin: the host runs ahead
+    outs = []
+    for i in range(12):
+        k = i % 2
+        with torch.cuda.stream(streams[k]):
+            y = y0.clone()
+            inst.apply(calls[k], x, y, wss[k], stream=streams[k])
+        outs.append((k, y))
+    torch.cuda.synchronize()
+    from heterogeneous_lora_amd import _lib
+    for k in range(2):
+        assert _lib.workspace_status(wss[k].data_ptr(), streams[k].cuda_stream) == 0
+    first = None
+    for i, (k, y) in enumerate(outs):
+        bits = y.cpu().numpy().view(np.uint16)
+        check_close(bits, ref, wl.dtype, f"two-stream call {i}")
+        first = bits if first is None else first
+        assert np.array_equal(bits, first), f"call {i} differs"

@@ -65,7 +65,13 @@ def test_pool_accounting_and_ownership():
     assert set(pt0[:24]).isdisjoint(pt1[:40])
     assert set(pt0[:24]) | set(pt1[:40]) == set(np.nonzero(own == 0)[0])
     pool.free_kv(kv[:10])
-    assert pool.info()["n_free"] == 512 - need0 - need5 - 27
+    assert pool.info()["n_free"] == 512 - need0 - need5 - 27 == pool.n_free()
+    pool.free(kv[10:12])  # the scope's name for returning pages: same rules as free_kv
+    assert pool.n_free() == 512 - need0 - need5 - 25
+    with pytest.raises(_lib.SloraError) as e:
+        pool.free(kv[10:11])  # already free
+    assert e.value.code == _lib.E_INVALID and pool.n_free() == 512 - need0 - need5 - 25
+    pool.alloc_kv(2)
     pool.free_adapter(0)
     assert (pool.owners() == 0).sum() == 0
     assert pool.info()["n_free"] == 512 - need5 - 27
