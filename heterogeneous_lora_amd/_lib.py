@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH):
         "slora_shrink": ([P, P, P, P, P, _c_i64, P], I),
         "slora_expand": ([P, P, P, P, P, _c_i64, P], I),
         "slora_apply": ([P, P, P, P, P, _c_i64, P], I),
+        "slora_apply_noalloc": ([P, P, P, P, P], I),
         "slora_plan_inspect": ([P, P, P, P, I, P], I),
         "slora_timing_enable": ([I], I),
         "slora_workspace_status": ([P, P, P], I),
@@ -237,6 +238,11 @@ def apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
                               _vp(ws), ws_bytes, _vp(stream)), "apply")
 
 
+def apply_noalloc(call: Call, x: int, y: int, stream: int):
+    _check(load().slora_apply_noalloc(ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(x),
+                                      _vp(y), _vp(stream)), "apply_noalloc")
+
+
 def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
     """slora_apply with its arguments converted once: returns a no-argument callable for
     callers that repeat the same call (same buffers, new contents) many times."""
@@ -284,9 +290,10 @@ def set_wait_limit(polls: int):
     _check(load().slora_set_wait_limit(polls), "set_wait_limit")
 
 
-def workspace_status(ws: int, stream: int) -> int:
+def workspace_status(ws: Optional[int], stream: int) -> int:
     """0 if every fused call on this workspace since the last status read ran clean;
-    1 if a wait gave up in one of them. Synchronizes the stream; clears the flag."""
+    1 if a wait gave up in one of them. Synchronizes the stream; clears the flag.
+    ws None: the current device's static scratch of apply_noalloc."""
     st = _c_i32()
     _check(load().slora_workspace_status(_vp(ws), _vp(stream), ctypes.byref(st)), "workspace_status")
     return st.value

@@ -54,6 +54,10 @@ struct Ring {
   // queued on that stream so far (one event, recorded only when the stream changes).
   hipStream_t fused_stream = nullptr;
   hipEvent_t fused_ev = nullptr;
+  // Allocation-free calls share the device's static scratch, so each of them is ordered
+  // after the previous one the same way, whatever kernels it runs.
+  hipStream_t shared_stream = nullptr;
+  hipEvent_t shared_ev = nullptr;
 };
 std::mutex g_mu;  // guards the rings, the epoch map and the timing state
 int32_t g_spin_limit = kDefaultSpinLimit;  // decode expand waves' bounded wait
@@ -98,15 +102,18 @@ int ring_init(Ring& ring) {
       const hipError_t e = hipEventCreateWithFlags(&g.ev, hipEventDisableTiming);
       if (e != hipSuccess) { g.ev = nullptr; return hip_fail(e, "staging: hipEventCreate"); }
     }
-  if (!ring.fused_ev) {
-    const hipError_t e = hipEventCreateWithFlags(&ring.fused_ev, hipEventDisableTiming);
-    if (e != hipSuccess) { ring.fused_ev = nullptr; return hip_fail(e, "hipEventCreate"); }
-  }
+  for (hipEvent_t* ev : {&ring.fused_ev, &ring.shared_ev})
+    if (!*ev) {
+      const hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+      if (e != hipSuccess) { *ev = nullptr; return hip_fail(e, "hipEventCreate"); }
+    }
   ring.ready = true;
   return SLORA_OK;
 }
 
-int acquire_slot(size_t n, hipStream_t stream, SlotRef* out) {
+// may_grow = false (allocation-free calls): a plan larger than the slot is an error
+// raised before the slot is taken.
+int acquire_slot(size_t n, hipStream_t stream, bool may_grow, SlotRef* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -114,6 +121,9 @@ int acquire_slot(size_t n, hipStream_t stream, SlotRef* out) {
   int rc = ring_init(ring);
   if (rc) return rc;
   const int i = ring.next;
+  if (!may_grow && ring.slot[i].cap < n)
+    return fail(SLORA_E_INVALID, "work list of %zu bytes exceeds the %zu-byte staging slot an "
+                "allocation-free call may use", n, ring.slot[i].cap);
   SlotGroup& grp = ring.grp[i / kGroup];
   if (i % kGroup == 0) {  // the group comes round again: its previous calls must be done
     if (grp.pending) {
@@ -232,8 +242,11 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
                 float* v_out, const float* v_in, void* y, void* ws, int64_t ws_bytes,
                 const WsLayout& lay, hipStream_t s, int mode, Ring* ring);
 
+// shared: ws is the device's static scratch (allocation-free calls): the call is
+// ordered after the previous such call and allocates nothing.
 int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out,
-        const float* v_in, void* y, void* ws, int64_t ws_bytes, void* stream, int mode) {
+        const float* v_in, void* y, void* ws, int64_t ws_bytes, void* stream, int mode,
+        bool shared = false) {
   clear_error();
   PlanView pv;
   const int64_t bytes = plan_bytes(L, R, &t_scratch, &pv);
@@ -256,8 +269,15 @@ int run(const slora_lora* L, const slora_routing* R, const void* x, float* v_out
   std::lock_guard<std::mutex> lk(g_mu);
   hipStream_t s = (hipStream_t)stream;
   SlotRef slot;
-  int rc = acquire_slot((size_t)bytes, s, &slot);
+  int rc = acquire_slot((size_t)bytes, s, !shared, &slot);
   if (rc) return rc;
+  if (shared) {
+    rc = order_after(&slot.ring->shared_stream, slot.ring->shared_ev, s);
+    if (rc) {
+      (void)release_slot(slot, s, false);
+      return rc;
+    }
+  }
   plan_write(L, R, &t_scratch, slot.host(), &pv);  // kernels read this host buffer directly
   rc = launch_plan(L, R, pv, x, v_out, v_in, y, ws, ws_bytes, lay, s, mode, slot.ring);
   const int rc2 = release_slot(slot, s, rc == SLORA_OK);
@@ -374,6 +394,13 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
 
 }  // namespace
 
+namespace slora {
+int apply_shared(const slora_lora* L, const slora_routing* R, const void* x, void* y, void* ws,
+                 int64_t ws_bytes, void* stream) {
+  return run(L, R, x, nullptr, nullptr, y, ws, ws_bytes, stream, kApply, true);
+}
+}  // namespace slora
+
 extern "C" {
 
 static int impl_slora_timing_enable(int32_t on) {
@@ -454,7 +481,15 @@ static int impl_slora_workspace_size(const slora_lora* lora, const slora_routing
 
 static int impl_slora_workspace_status(void* ws, void* stream, int32_t* status) {
   clear_error();
-  if (!ws || !status) return fail(SLORA_E_INVALID, "workspace_status: NULL argument");
+  if (!status) return fail(SLORA_E_INVALID, "workspace_status: status is NULL");
+  if (!ws) {  // the current device's static scratch (allocation-free calls)
+    const int rc = shared_scratch(&ws, nullptr);
+    if (rc) return rc;
+    if (!ws) {  // no allocation-free call has set it up on this device: nothing to report
+      *status = 0;
+      return SLORA_OK;
+    }
+  }
   unsigned long long flag = 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(&flag, ws, sizeof flag, hipMemcpyDeviceToHost, s);

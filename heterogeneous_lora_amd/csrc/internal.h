@@ -130,6 +130,15 @@ struct WsLayout {
 };
 WsLayout ws_layout(const slora_lora* L, const slora_routing* R);
 
+// slora_apply on the current device's static scratch (api.cpp): ordered after the previous
+// such call on the device, and a plan that would need a larger staging slot is an error.
+int apply_shared(const slora_lora* L, const slora_routing* R, const void* x, void* y, void* ws,
+                 int64_t ws_bytes, void* stream);
+// The current device's static scratch (noalloc.hip): *ptr its device address, or nullptr
+// when no allocation-free call has resolved it on this device yet; *bytes its size.
+// Resolves nothing itself.
+int shared_scratch(void** ptr, int64_t* bytes);
+
 // ---------------------------------------------------------------- launchers
 // Optional HIP events that the launch itself records at the kernel's start and end
 // (hipExtLaunchKernel), so a timed interval holds the kernel and nothing else.

@@ -219,12 +219,30 @@ int slora_expand(const slora_lora* lora, const slora_routing* routing, const flo
 int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
                 void* ws, int64_t ws_bytes, void* stream);
 
+/* slora_apply for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments minus
+ * the workspace, same kernels, same results bit for bit. The workspace is a static
+ * device array of the library, 64 MiB on every GPU it runs on, held until the process
+ * ends; a call that needs more (ws_layout: 256 + n_tokens * r_max * 8 bytes + the
+ * prefill partial sums) is refused with SLORA_E_INVALID before anything runs, and so is
+ * one whose work list would outgrow its 1 MiB staging slot. The call allocates no
+ * device or pinned memory, except on its first call on a device, which also creates the
+ * library's staging ring if no compute call has yet, resolves the array's address and
+ * clears the array on `stream`. Every call on a GPU shares that GPU's array, which keeps
+ * the last call's contents; the library orders the calls it is given (a call on another
+ * stream than the previous one first waits for that stream's queued work), so calls
+ * that overlap on one GPU (another process, or work outside the library writing the
+ * array) race. Give-ups are read with slora_workspace_status(NULL, ...). */
+int slora_apply_noalloc(const slora_lora* lora, const slora_routing* routing, const void* x,
+                        void* y, void* stream);
+
 /* Status of the slora_apply calls that used workspace ws since the previous status
  * read, once the work on `stream` has finished (this call synchronizes the stream):
  * 0 = clean; 1 = in at least one of them a decode workgroup gave up waiting for v
  * that another workgroup of the same launch should have published (that call's
  * results are not valid). The give-up is sticky in the workspace header until this
- * call reads it, and reading clears it. */
+ * call reads it, and reading clears it. ws = NULL reads the current device's static
+ * scratch of slora_apply_noalloc (0 if no such call has run on it). */
 int slora_workspace_status(void* ws, void* stream, int32_t* status);
 
 /* Bound of the wait in decode launches: an expand wave polls for its v at most `polls`
