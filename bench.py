@@ -293,7 +293,7 @@ def pct(a, q):
     return round(float(np.percentile(np.asarray(a), q)), 3) if len(a) else None
 
 
-def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev):
+def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev, overlap_steps=0):
     """Time `steps` steps (one apply per projection, rotating over n_inst instances) after
     `warmup` untimed ones. Returns the measured figures; exits non-zero if a fused call's
     wait gave up in any of them (its results would not be valid)."""
@@ -355,6 +355,42 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev)
     _lib.timing_enable(False)
     torch.cuda.synchronize()
     pnames, pms = _lib.timing_read_all()
+    overlap = None
+    if overlap_steps and len(insts) >= 2:
+        # apply kernels while an adapter fetch runs on a side stream: the last instance's
+        # adapters are fetched again (same bytes into its own pages) while the other
+        # instances run overlap_steps steps with every launch timed
+        tgt = insts[-1][0]
+        side = torch.cuda.Stream(device=dev)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        side.wait_stream(stream)
+        f0.record(side)
+        for a in tgt.adapters:
+            at, bb = tgt.store.ptrs(a, n_proj)
+            tgt.pool.fetch_async(a, at, bb, side.cuda_stream, None)
+        f1.record(side)
+        _lib.timing_enable(True)
+        t2 = time.perf_counter()
+        for i in range(overlap_steps):
+            for run in bound[i % (len(bound) - 1)]:
+                run()
+        _lib.timing_enable(False)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        onames, oms = _lib.timing_read_all()
+        f_ms = f0.elapsed_time(f1)
+        dom_o = max(set(onames), key=lambda k: sum(m for n, m in zip(onames, oms) if n == k))
+        during = np.array([m for n, m in zip(onames, oms) if n == dom_o]) * 1e3
+        alone = np.array([m for n, m in zip(pnames, pms) if n == dom_o]) * 1e3
+        overlap = {"kernel": dom_o, "steps": overlap_steps,
+                   "apply_us_p50_alone": pct(alone, 50), "apply_us_p50_during_fetch": pct(during, 50),
+                   "apply_us_p90_during_fetch": pct(during, 90),
+                   "step_us_during_fetch": round((t3 - t2) / overlap_steps * 1e6, 2),
+                   "fetch_bytes": fetch_bytes, "fetch_ms": round(f_ms, 3),
+                   "fetch_gbps_during_apply": round(fetch_bytes / (f_ms * 1e-3) / 1e9, 2),
+                   "steps_inside_fetch": int(min(overlap_steps, f_ms * 1e-3 / max((t3 - t2) / overlap_steps, 1e-9)))}
+        log(f"[bench] apply during a side-stream fetch: {json.dumps(overlap)}")
     bad = [i for i, (_, _, _, ws) in enumerate(insts) if _lib.workspace_status(ws.data_ptr(), stream.cuda_stream)]
     if bad:
         print(f"bench.py: a decode launch gave up waiting in instance(s) {bad}: results invalid",
@@ -390,7 +426,7 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev)
                step_algorithmic_gbps=round(step_bytes / kern_total_s / 1e9, 1),
                fetch={"bytes": fetch_bytes, "ms": round(fms, 3),
                       "gbps": round(fetch_bytes / (fms * 1e-3) / 1e9, 2)},
-               active=len(active), workspace_status="clean")
+               active=len(active), workspace_status="clean", fetch_overlap=overlap)
     for inst, *_ in insts:
         inst.close()
     return out
@@ -424,6 +460,8 @@ def main():
                     help="decode_7b only: skip the prefill_sgmv sub-record")
     ap.add_argument("--pct-steps", type=int, default=64,
                     help="extra steps, every launch timed, for the p10/p50/p90 kernel durations")
+    ap.add_argument("--overlap-steps", type=int, default=64,
+                    help="steps timed while a side-stream adapter fetch runs (0: skip)")
     ap.add_argument("--event-every", type=int, default=4,
                     help="time the kernels of one step in this many with HIP events")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
@@ -459,7 +497,7 @@ def main():
     dinfo = device_info()
     log(f"[bench] device: {dinfo}")
     main_run = run_workload(wl, policy, args.instances, args.steps, args.warmup, args.event_every,
-                            args.pct_steps, dev)
+                            args.pct_steps, dev, overlap_steps=args.overlap_steps)
     roofline = roofline_of(main_run["kernels"], wl.name)
     copy_ref = copy_reference(dev)
     roofline["copy_gbps"] = copy_ref["gbps"]
@@ -511,6 +549,7 @@ def main():
         "workspace_status": main_run["workspace_status"],
         "copy_reference": copy_ref,
         "fetch": fetch,
+        "fetch_overlap": main_run["fetch_overlap"],
         "prefill": prefill,
         "device": dinfo,
     }

@@ -43,6 +43,28 @@ class Routing(ctypes.Structure):
                 ("seg_adapter", _vp), ("token_adapter", _vp), ("policy", _c_i32)]
 
 
+class ResidencyStats(ctypes.Structure):
+    _fields_ = [("resident", _c_i32), ("pinned", _c_i32), ("hits", _c_i64), ("misses", _c_i64),
+                ("evictions", _c_i64), ("prefetches", _c_i64)]
+
+
+class SchedConfig(ctypes.Structure):
+    _fields_ = [("kv_pages_per_token", _c_i32), ("max_batch_tokens", _c_i32),
+                ("max_running", _c_i32)]
+
+
+class SchedBatch(ctypes.Structure):
+    _fields_ = [("step", _c_i64), ("n_tokens", _c_i32), ("n_segments", _c_i32),
+                ("seg_offsets", _vp), ("seg_adapter", _vp), ("token_adapter", _vp),
+                ("seg_request", _vp), ("token_request", _vp),
+                ("n_fetch", _c_i32), ("fetch", _vp), ("n_evicted", _c_i32), ("evicted", _vp),
+                ("n_finished", _c_i32), ("finished", _vp), ("n_aborted", _c_i32), ("aborted", _vp),
+                ("abort_reason", _vp), ("n_waiting", _c_i32), ("n_running", _c_i32),
+                ("free_pages", _c_i64)]
+
+
+ABORT_DEADLINE, ABORT_POOL_FULL = 1, 2
+
 _lib = None
 
 
@@ -88,6 +110,19 @@ def load(path: str = LIB_PATH):
         "slora_timing_read": ([I, P, P], I),
         "slora_timing_read_all": ([_c_i64, P, P, P], I),
         "slora_set_wait_limit": ([I], I),
+        "slora_residency_create": ([P, I, P, P, P], I),
+        "slora_residency_destroy": ([P], I),
+        "slora_residency_acquire": ([P, I, I, P, P, I, P], I),
+        "slora_residency_prefetch": ([P, I, I, P], I),
+        "slora_residency_release": ([P, I], I),
+        "slora_residency_info": ([P, P], I),
+        "slora_residency_is_resident": ([P, I, P], I),
+        "slora_sched_create": ([P, P, P, P], I),
+        "slora_sched_destroy": ([P], I),
+        "slora_sched_submit": ([P, _c_i64, I, I, I, I, _c_i64], I),
+        "slora_sched_finish": ([P, _c_i64], I),
+        "slora_sched_step": ([P, P], I),
+        "slora_sched_request_pages": ([P, _c_i64, P, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -186,6 +221,112 @@ class Pool:
         _check(self._lib.slora_fetch_async(self.handle, adapter_id, at, b, ctypes.c_void_p(stream),
                                            ctypes.c_void_p(event) if event else None),
                "fetch_async")
+
+
+class Residency:
+    """slora_residency: LRU residency of the adapters of one pool (host bookkeeping)."""
+
+    def __init__(self, pool: Pool, d_in: Sequence[int], d_out: Sequence[int]):
+        self._lib = load()
+        self.pool = pool
+        di = np.ascontiguousarray(d_in, np.int32)
+        do = np.ascontiguousarray(d_out, np.int32)
+        h = ctypes.c_void_p()
+        _check(self._lib.slora_residency_create(pool.handle, di.size, _p(di), _p(do), ctypes.byref(h)),
+               "residency_create")
+        self.handle = h
+
+    def destroy(self):
+        if self.handle:
+            _check(self._lib.slora_residency_destroy(self.handle), "residency_destroy")
+            self.handle = None
+
+    def acquire(self, adapter_id: int, rank: int):
+        """(needs_fetch, [evicted ids])."""
+        nf, ne = _c_i32(), _c_i32()
+        ev = np.zeros(4096, np.int32)
+        _check(self._lib.slora_residency_acquire(self.handle, adapter_id, rank, ctypes.byref(nf), _p(ev),
+                                                 ev.size, ctypes.byref(ne)), "residency_acquire")
+        return bool(nf.value), [int(v) for v in ev[:ne.value]]
+
+    def prefetch(self, adapter_id: int, rank: int) -> bool:
+        nf = _c_i32()
+        _check(self._lib.slora_residency_prefetch(self.handle, adapter_id, rank, ctypes.byref(nf)),
+               "residency_prefetch")
+        return bool(nf.value)
+
+    def release(self, adapter_id: int):
+        _check(self._lib.slora_residency_release(self.handle, adapter_id), "residency_release")
+
+    def info(self) -> dict:
+        st = ResidencyStats()
+        _check(self._lib.slora_residency_info(self.handle, ctypes.byref(st)), "residency_info")
+        return {f: getattr(st, f) for f, _ in ResidencyStats._fields_}
+
+    def pins(self, adapter_id: int) -> int:
+        """Pin count, -1 if not resident."""
+        v = _c_i32()
+        _check(self._lib.slora_residency_is_resident(self.handle, adapter_id, ctypes.byref(v)),
+               "residency_is_resident")
+        return v.value
+
+
+def _arr(ptr, n, dtype):
+    if n <= 0 or not ptr:
+        return np.zeros(0, dtype)
+    ct = ctypes.c_int64 if dtype == np.int64 else ctypes.c_int32
+    return np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ct)), shape=(n,)).copy()
+
+
+class Scheduler:
+    """slora_sched: FIFO continuous-batching admission over the unified pool."""
+
+    def __init__(self, pool: Pool, residency: Optional[Residency], kv_pages_per_token: int,
+                 max_batch_tokens: int, max_running: int):
+        self._lib = load()
+        self.pool, self.residency = pool, residency
+        cfg = SchedConfig(kv_pages_per_token, max_batch_tokens, max_running)
+        h = ctypes.c_void_p()
+        _check(self._lib.slora_sched_create(pool.handle, residency.handle if residency else None,
+                                            ctypes.byref(cfg), ctypes.byref(h)), "sched_create")
+        self.handle = h
+
+    def destroy(self):
+        if self.handle:
+            _check(self._lib.slora_sched_destroy(self.handle), "sched_destroy")
+            self.handle = None
+
+    def submit(self, request_id: int, adapter_id: int, rank: int, prompt_len: int,
+               max_new_tokens: int, deadline_step: int = -1):
+        _check(self._lib.slora_sched_submit(self.handle, request_id, adapter_id, rank, prompt_len,
+                                            max_new_tokens, deadline_step), "sched_submit")
+
+    def finish(self, request_id: int):
+        _check(self._lib.slora_sched_finish(self.handle, request_id), "sched_finish")
+
+    def step(self) -> dict:
+        b = SchedBatch()
+        _check(self._lib.slora_sched_step(self.handle, ctypes.byref(b)), "sched_step")
+        S = b.n_segments
+        so = _arr(b.seg_offsets, S + 1, np.int32)
+        n_dec = b.n_tokens - int(so[-1])
+        return dict(step=b.step, n_tokens=b.n_tokens, seg_offsets=so,
+                    seg_adapter=_arr(b.seg_adapter, S, np.int32),
+                    token_adapter=_arr(b.token_adapter, n_dec, np.int32),
+                    seg_request=_arr(b.seg_request, S, np.int64),
+                    token_request=_arr(b.token_request, n_dec, np.int64),
+                    fetch=_arr(b.fetch, b.n_fetch, np.int32), evicted=_arr(b.evicted, b.n_evicted, np.int32),
+                    finished=_arr(b.finished, b.n_finished, np.int64),
+                    aborted=_arr(b.aborted, b.n_aborted, np.int64),
+                    abort_reason=_arr(b.abort_reason, b.n_aborted, np.int32),
+                    n_waiting=b.n_waiting, n_running=b.n_running, free_pages=b.free_pages)
+
+    def request_pages(self, request_id: int) -> np.ndarray:
+        n = _c_i32()
+        buf = np.zeros(1 << 20, np.int32)
+        _check(self._lib.slora_sched_request_pages(self.handle, request_id, _p(buf), buf.size,
+                                                   ctypes.byref(n)), "sched_request_pages")
+        return buf[:n.value].copy()
 
 
 class Call:

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build", "slora")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HOST_SRCS = ["pool.cpp", "plan.cpp", "api.cpp"]
+HOST_SRCS = ["pool.cpp", "plan.cpp", "api.cpp", "sched.cpp"]
 DEVICE_SRCS = ["mbgmv.hip", "sgmv.hip", "fetch.hip", "noalloc.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

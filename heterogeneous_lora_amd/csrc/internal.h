@@ -139,6 +139,14 @@ int apply_shared(const slora_lora* L, const slora_routing* R, const void* x, voi
 // Resolves nothing itself.
 int shared_scratch(void** ptr, int64_t* bytes);
 
+// ---------------------------------------------------------------- pool queries (pool.cpp)
+// Pages adapter `id` holds (0 if not resident) and whether a fetch into it may still be
+// in flight (its event not yet complete). Host only; returns SLORA_OK or an error code.
+int pool_adapter_state(const slora_pool* pool, int32_t id, int64_t* pages, bool* busy);
+// Pages an adapter of this rank would take for projections d_in[p] x d_out[p].
+int64_t pool_adapter_need(const slora_pool* pool, int32_t rank, int32_t n_proj, const int32_t* d_in,
+                          const int32_t* d_out);
+
 // ---------------------------------------------------------------- launchers
 // Optional HIP events that the launch itself records at the kernel's start and end
 // (hipExtLaunchKernel), so a timed interval holds the kernel and nothing else.

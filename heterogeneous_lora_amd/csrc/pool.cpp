@@ -88,6 +88,32 @@ struct slora_pool {
   std::map<int32_t, AdapterRec> adapters;
 };
 
+namespace slora {
+
+int pool_adapter_state(const slora_pool* pool, int32_t id, int64_t* pages, bool* busy) {
+  *pages = 0;
+  *busy = false;
+  auto it = pool->adapters.find(id);
+  if (it == pool->adapters.end()) return SLORA_OK;
+  for (const auto& pg : it->second.pages) *pages += (int64_t)pg.size();
+  if (it->second.ev && it->second.fetch_recorded) {
+    const hipError_t e = hipEventQuery(it->second.ev);
+    if (e == hipErrorNotReady) *busy = true;
+    else if (e != hipSuccess) return hip_fail(e, "hipEventQuery");
+  }
+  return SLORA_OK;
+}
+
+int64_t pool_adapter_need(const slora_pool* pool, int32_t rank, int32_t n_proj, const int32_t* d_in,
+                          const int32_t* d_out) {
+  int64_t need = 0;
+  for (int32_t p = 0; p < n_proj; ++p)
+    need += (int64_t)rank * ((d_in[p] + pool->P - 1) / pool->P + (d_out[p] + pool->P - 1) / pool->P);
+  return need;
+}
+
+}  // namespace slora
+
 extern "C" {
 
 const char* slora_last_error(void) { return t_error.c_str(); }

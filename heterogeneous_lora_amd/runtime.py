@@ -8,6 +8,7 @@ benchmark.
 
 from __future__ import annotations
 
+from dataclasses import replace as dataclass_replace
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -162,4 +163,89 @@ class PagedLoRA:
 
     def close(self):
         torch.cuda.synchronize(self.device)
+        self.pool.destroy()
+
+
+class ServingLoop:
+    """Continuous batching of one projection over a unified pool: slora_sched admits
+    requests FIFO by free pages, slora_residency keeps adapters resident (LRU eviction),
+    adapters a step needs are fetched on a side stream from the host store, and the
+    step's batch (new prompts as segments, one decode token per running request) runs
+    through slora_apply on the compute stream once the fetch event has fired.
+
+    Every adapter the workload defines is in the host store; only the pool's pages limit
+    how many are resident at once. The weights, x and y0 of a step are seeded synthetic
+    data (the same generators the tests and the oracle use)."""
+
+    def __init__(self, wl, n_pages: int, kv_pages_per_token: int = 2, max_batch_tokens: int = 4096,
+                 max_running: int = 512, proj: int = 0, device: str = "cuda", seed: int = 0):
+        self.wl, self.proj, self.device = wl, proj, torch.device(device)
+        p = wl.projections[proj]
+        self.d_in, self.d_out = p.d_in, p.d_out
+        self.n_pages = n_pages
+        P = wl.page_elems
+        self.pool_t = torch.full((n_pages * P,), SENTINEL_I16[wl.dtype], dtype=torch.int16,
+                                 device=self.device)
+        self.pool = _lib.Pool(self.pool_t.data_ptr(), n_pages, P, wl.dtype, seed)
+        self.res = _lib.Residency(self.pool, [p.d_in], [p.d_out])
+        self.sched = _lib.Scheduler(self.pool, self.res, kv_pages_per_token, max_batch_tokens,
+                                    max_running)
+        # the projection alone (its weights are drawn as projection 0 of this workload)
+        self.one = dataclass_replace(wl, projections=[p], _cache={})
+        self.store = HostStore(self.one, list(range(wl.n_adapters)))
+        self.side = torch.cuda.Stream(device=self.device)
+        self.stream = torch.cuda.current_stream(self.device)
+        self.scales = wl.scales.astype(np.float32)
+        self.r_max = max(int(wl.ranks.max()), 1)
+        self.fetch_bytes = 0
+        self.steps_run = 0
+
+    def submit(self, request_id, adapter_id, prompt_len, max_new_tokens, deadline_step=-1):
+        r = int(self.wl.ranks[adapter_id]) if adapter_id >= 0 else 0
+        self.sched.submit(request_id, adapter_id, r, prompt_len, max_new_tokens, deadline_step)
+
+    def step(self, seed: int):
+        """Plan one step, fetch what it needs, run its batch. Returns (batch dict, x, y0, y)
+        as host arrays (uint16 bits) for checking, or the batch alone when it is empty."""
+        b = self.sched.step()
+        if b["fetch"].size:
+            done = torch.cuda.Event()
+            self.side.wait_stream(self.stream)
+            for a in b["fetch"]:
+                at, bb = self.store.ptrs(int(a), 1)
+                self.pool.fetch_async(int(a), at, bb, self.side.cuda_stream, None)
+                self.fetch_bytes += int(self.wl.ranks[int(a)]) * (self.d_in + self.d_out) * 2
+            done.record(self.side)
+            self.stream.wait_event(done)
+        if b["n_tokens"] == 0:
+            return b, None, None, None
+        pt, base, rank = self.pool.page_table(0, self.wl.n_adapters)
+        pt_dev = torch.from_numpy(np.ascontiguousarray(pt)).to(self.device) if pt.size else \
+            torch.zeros(1, dtype=torch.int32, device=self.device)
+        T = b["n_tokens"]
+        rng_x = np.random.default_rng([seed, 1])
+        rng_y = np.random.default_rng([seed, 2])
+        from workloads import normal_bits
+        x = normal_bits(rng_x, (T, self.d_in), 1.0, self.wl.dtype)
+        y0 = normal_bits(rng_y, (T, self.d_out), 1.0, self.wl.dtype)
+        call = _lib.Call(pool_ptr=self.pool_t.data_ptr(), n_pages=self.n_pages,
+                         page_elems=self.wl.page_elems, dtype=self.wl.dtype, d_in=self.d_in,
+                         d_out=self.d_out, page_table_ptr=pt_dev.data_ptr(), page_table_len=pt.size,
+                         base=base, rank=self.wl.ranks, scale=self.scales, r_max=self.r_max,
+                         n_tokens=T, seg_offsets=b["seg_offsets"], seg_adapter=b["seg_adapter"],
+                         token_adapter=b["token_adapter"])
+        xd = _dev_i16(x, self.device)
+        yd = _dev_i16(y0, self.device)
+        ws = torch.zeros(_lib.workspace_size(call), dtype=torch.uint8, device=self.device)
+        _lib.apply(call, xd.data_ptr(), yd.data_ptr(), ws.data_ptr(), ws.numel(), self.stream.cuda_stream)
+        status = _lib.workspace_status(ws.data_ptr(), self.stream.cuda_stream)
+        if status:
+            raise RuntimeError(f"step {b['step']}: a decode launch gave up waiting")
+        self.steps_run += 1
+        return b, x, y0, yd.cpu().numpy().view(np.uint16)
+
+    def close(self):
+        torch.cuda.synchronize(self.device)
+        self.sched.destroy()
+        self.res.destroy()
         self.pool.destroy()

@@ -156,6 +156,121 @@ int slora_pool_owners(const slora_pool* pool, int32_t* owner);
 int slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
                       const void* const* host_B, void* side_stream, void* done_event);
 
+/* ------------------------------------------------------------------ adapter residency
+ * All adapters stay in host memory; those running requests use are fetched to the pool
+ * on demand (review, abstract and "Proposed method"), and when the active set outgrows
+ * the pool adapters are swapped over PCIe ("Makale Bulteni - S-LoRA", section "Iddia
+ * ve Gerceklik": thrashing shows in the tail latency). A residency manager owns the
+ * adapters of one pool (the caller must not allocate or free adapters of that pool
+ * itself): each resident adapter has a pin count (pinned = in use); acquiring an
+ * adapter that is not resident allocates its pages, evicting unpinned adapters in
+ * least-recently-used order when the free list is short (never one whose fetch may
+ * still be in flight; recency = the adapter's last release or its prefetch), and
+ * reports that the caller must fetch it (slora_fetch_async)
+ * before any compute call reads it. Page tables change with every allocation or
+ * eviction: export them again (slora_pool_page_table) before the next compute call.
+ * Host only; a manager is not thread-safe. */
+typedef struct slora_residency slora_residency;
+typedef struct {
+  int32_t resident, pinned;  /* adapters resident now, and pinned among them */
+  int64_t hits, misses;      /* acquires that found the adapter resident / had to allocate it */
+  int64_t evictions, prefetches;
+} slora_residency_stats;
+
+/* A manager for `pool`; every adapter has n_proj projections d_in[p] x d_out[p]. */
+int slora_residency_create(slora_pool* pool, int32_t n_proj, const int32_t* d_in,
+                           const int32_t* d_out, slora_residency** out);
+/* Frees the manager (not the adapters: they stay resident in the pool). */
+int slora_residency_destroy(slora_residency* res);
+
+/* Pin adapter `adapter_id` of rank `rank` for use. *needs_fetch = 1 when it was not
+ * resident and its pages were just allocated (fetch before use), else 0. Adapters
+ * evicted to make room are written to evicted[evicted_cap] (*n_evicted of them).
+ * SLORA_E_POOL_FULL, with nothing evicted or allocated, when free pages plus the pages
+ * of evictable adapters are not enough. SLORA_E_INVALID when it is resident with
+ * another rank. */
+int slora_residency_acquire(slora_residency* res, int32_t adapter_id, int32_t rank,
+                            int32_t* needs_fetch, int32_t* evicted, int32_t evicted_cap,
+                            int32_t* n_evicted);
+/* Make an adapter resident ahead of use without pinning it, only if the free list holds
+ * its pages (evicts nothing); *needs_fetch = 1 when it was allocated now. */
+int slora_residency_prefetch(slora_residency* res, int32_t adapter_id, int32_t rank,
+                             int32_t* needs_fetch);
+/* Unpin (SLORA_E_STATE if not pinned); at zero pins the adapter becomes evictable. */
+int slora_residency_release(slora_residency* res, int32_t adapter_id);
+int slora_residency_info(const slora_residency* res, slora_residency_stats* stats);
+/* *pins = the adapter's pin count, or -1 when it is not resident. */
+int slora_residency_is_resident(const slora_residency* res, int32_t adapter_id, int32_t* pins);
+
+/* ------------------------------------------------------------------ admission
+ * Continuous batching over the unified pool (the continuous-batching page, sections
+ * "Surekli Gruplama (Continuous Batching) Nedir ve Nasil Calisir?" and "vLLM
+ * Zamanlayicisi: Istekleri Dinamik Olarak Yonetme"; review, "Proposed method": early-
+ * abort scheduling on the unified pool). Requests wait in a FIFO queue. Each step:
+ *   1. running requests that produced max_new_tokens leave (their KV pages are freed,
+ *      their adapter unpinned); waiting or running requests past their deadline step
+ *      are aborted the same way (SLORA_ABORT_DEADLINE);
+ *   2. every running request decodes one token and takes kv_pages_per_token more KV
+ *      pages; while the pool cannot give them all, the most recently admitted running
+ *      request is aborted (SLORA_ABORT_POOL_FULL);
+ *   3. waiting requests are admitted in order while the step's token budget
+ *      (max_batch_tokens), max_running and the pool (the prompt's KV pages, and the
+ *      adapter's pages through the residency manager, evicting unpinned adapters) allow;
+ *      the first that does not fit stops admission. Its prompt is the step's prefill.
+ * The step's batch is a ready slora_routing: admitted prompts as segments, then one
+ * decode token per running request. One token's KV takes kv_pages_per_token pages of
+ * the pool (a page holds one token's K or V vector for one layer). */
+typedef struct slora_sched slora_sched;
+typedef struct {
+  int32_t kv_pages_per_token; /* >= 1 */
+  int32_t max_batch_tokens;   /* tokens per step (prefill + decode), >= max_running */
+  int32_t max_running;        /* running requests at most, >= 1 */
+} slora_sched_config;
+#define SLORA_ABORT_DEADLINE 1  /* the request's deadline step passed */
+#define SLORA_ABORT_POOL_FULL 2 /* its next token's KV pages did not fit the pool */
+/* One step's batch. Every pointer points into the scheduler and stays valid until its
+ * next step or destroy. */
+typedef struct {
+  int64_t step;
+  int32_t n_tokens, n_segments;
+  const int32_t* seg_offsets;     /* [n_segments + 1] */
+  const int32_t* seg_adapter;     /* [n_segments] */
+  const int32_t* token_adapter;   /* [n_tokens - seg_offsets[n_segments]] */
+  const int64_t* seg_request;     /* request of each segment */
+  const int64_t* token_request;   /* request of each decode token */
+  int32_t n_fetch;                /* adapters allocated this step: fetch before the compute call */
+  const int32_t* fetch;
+  int32_t n_evicted;              /* adapters evicted this step */
+  const int32_t* evicted;
+  int32_t n_finished;             /* requests that left this step, done */
+  const int64_t* finished;
+  int32_t n_aborted;              /* requests aborted this step, with the reason of each */
+  const int64_t* aborted;
+  const int32_t* abort_reason;
+  int32_t n_waiting, n_running;   /* after the step */
+  int64_t free_pages;             /* of the pool, after the step */
+} slora_sched_batch;
+
+/* A scheduler over `pool`; `res` (may be NULL: adapters are then the caller's
+ * business) manages the adapters requests use. */
+int slora_sched_create(slora_pool* pool, slora_residency* res, const slora_sched_config* cfg,
+                       slora_sched** out);
+/* Frees the running requests' KV pages and unpins their adapters, then the scheduler. */
+int slora_sched_destroy(slora_sched* sched);
+/* Queue a request: adapter_id (-1 = none) of rank `rank`, a prompt of prompt_len tokens
+ * (<= max_batch_tokens), at most max_new_tokens output tokens, aborted once a step past
+ * deadline_step begins (-1 = no deadline). SLORA_E_STATE if the id is queued or running. */
+int slora_sched_submit(slora_sched* sched, int64_t request_id, int32_t adapter_id, int32_t rank,
+                       int32_t prompt_len, int32_t max_new_tokens, int64_t deadline_step);
+/* The request is done now (an end-of-sequence token, or the client went away): if
+ * running, its KV pages are freed and its adapter unpinned; if waiting, it is dropped. */
+int slora_sched_finish(slora_sched* sched, int64_t request_id);
+/* Plan the next step (see above) into *batch. */
+int slora_sched_step(slora_sched* sched, slora_sched_batch* batch);
+/* KV pages a running request holds, in allocation order (pages[cap], *n of them). */
+int slora_sched_request_pages(const slora_sched* sched, int64_t request_id, int32_t* pages,
+                              int32_t cap, int32_t* n);
+
 /* ------------------------------------------------------------------ compute */
 
 /* One projection of the batch. All pointers are read only. */
