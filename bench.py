@@ -293,7 +293,8 @@ def pct(a, q):
     return round(float(np.percentile(np.asarray(a), q)), 3) if len(a) else None
 
 
-def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev, overlap_steps=0):
+def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev, overlap_steps=0,
+                 variant="paged"):
     """Time `steps` steps (one apply per projection, rotating over n_inst instances) after
     `warmup` untimed ones. Returns the measured figures; exits non-zero if a fused call's
     wait gave up in any of them (its results would not be valid)."""
@@ -308,19 +309,21 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     host_io = [(wl.x(p), wl.y0(p)) for p in range(n_proj)]
     insts, fetch_ms = [], []
     for i in range(n_inst):
-        inst = runtime.PagedLoRA(wl, device=dev, store=store, pool_seed=wl.pool_seed + i)
+        inst = runtime.PagedLoRA(wl, device=dev, store=store, pool_seed=wl.pool_seed + i,
+                                 ordered=variant == "split")
         fetch_ms.append(inst.fetch_ms)
         calls = [inst.call(p, policy) for p in range(n_proj)]
         io = [(runtime._dev_i16(x, inst.device), runtime._dev_i16(y0, inst.device)) for x, y0 in host_io]
-        ws = torch.zeros(max(_lib.workspace_size(c) for c in calls), dtype=torch.uint8, device=dev)
+        wsize = _lib.gathered_workspace_size if variant == "gathered" else _lib.workspace_size
+        ws = torch.zeros(max(wsize(c) for c in calls), dtype=torch.uint8, device=dev)
         insts.append((inst, calls, io, ws))
         log(f"[bench] instance {i} ready (fetch {inst.fetch_ms:.2f} ms)")
     del host_io
     fetch_bytes = sum(int(wl.ranks[a]) * (p.d_in + p.d_out) * 2 for a in active for p in wl.projections)
 
     stream = torch.cuda.current_stream(dev)
-    bound = [[inst.bind_apply(calls[p], io[p][0], io[p][1], ws, stream) for p in range(n_proj)]
-             for inst, calls, io, ws in insts]
+    bound = [[inst.bind_apply(calls[p], io[p][0], io[p][1], ws, stream, gathered=variant == "gathered")
+              for p in range(n_proj)] for inst, calls, io, ws in insts]
 
     def step(i):
         for run in bound[i % len(bound)]:
@@ -391,7 +394,9 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
                    "fetch_gbps_during_apply": round(fetch_bytes / (f_ms * 1e-3) / 1e9, 2),
                    "steps_inside_fetch": int(min(overlap_steps, f_ms * 1e-3 / max((t3 - t2) / overlap_steps, 1e-9)))}
         log(f"[bench] apply during a side-stream fetch: {json.dumps(overlap)}")
-    bad = [i for i, (_, _, _, ws) in enumerate(insts) if _lib.workspace_status(ws.data_ptr(), stream.cuda_stream)]
+    # (the gathered variant runs no decode launch that waits, and its workspace has no header)
+    bad = [] if variant == "gathered" else [
+        i for i, (_, _, _, ws) in enumerate(insts) if _lib.workspace_status(ws.data_ptr(), stream.cuda_stream)]
     if bad:
         print(f"bench.py: a decode launch gave up waiting in instance(s) {bad}: results invalid",
               file=sys.stderr)
@@ -405,8 +410,10 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     for k in sorted(set(names)):
         d = np.array([m for n, m in zip(names, ms) if n == k])
         dp = np.array([m for n, m in zip(pnames, pms) if n == k]) * 1e3
-        per_launch_bytes = float(np.mean([a[k]["bytes"] for a in alg]))
-        per_launch_flops = float(np.mean([a[k]["flops"] for a in alg]))
+        # the paged kernels' algorithmic work; the gathered variant's copy and its padded
+        # products have no such figure of their own (0)
+        per_launch_bytes = float(np.mean([a[k]["bytes"] if variant == "paged" and k in a else 0 for a in alg]))
+        per_launch_flops = float(np.mean([a[k]["flops"] if variant == "paged" and k in a else 0 for a in alg]))
         avg_s = float(d.mean()) * 1e-3
         kernels[k] = {"launches": int(d.size), "avg_us": round(avg_s * 1e6, 3),
                       "p10_us": pct(dp, 10), "p50_us": pct(dp, 50), "p90_us": pct(dp, 90),
@@ -417,6 +424,8 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     n_timed = (steps + ev - 1) // ev
     kern_total_s = float(np.sum(ms)) * 1e-3 / n_timed
     step_bytes = sum(kv["algorithmic_bytes"] * kv["launches"] for kv in kernels.values()) / n_timed
+    if variant != "paged":  # the same function: the paged path's algorithmic bytes per step
+        step_bytes = sum(a[f]["bytes"] for a in alg for f in ("mbgmv_fused", "sgmv_shrink", "sgmv_expand"))
     log(f"[bench] kernels: {json.dumps(kernels)}")
     log(f"[bench] all kernels of a step: {kern_total_s * 1e6:.1f} us, "
         f"{step_bytes / kern_total_s / 1e9:.0f} GB/s algorithmic")
@@ -430,6 +439,70 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     for inst, *_ in insts:
         inst.close()
     return out
+
+
+def capacity_ablation(steps=400, seed=0, fractions=(0.25, 0.5, 0.75)):
+    """Unified paging against separate adapter and KV memory (host simulation of the
+    scheduler, no GPU): the same request trace through slora_sched with one pool of
+    196,608 pages (the mixed 13B batch's pool, 5120-element pages) holding adapters and
+    KV, and with the same pages split into an adapter pool and a KV pool. A layer's
+    q/k/v/o adapters take rank x 8 pages, a token's KV 2 pages (K and V of one layer).
+    Requests arrive Poisson(24) per step, adapters Zipf(0.8) over 2000 with ranks U{8..128},
+    prompts U{16..256}, outputs U{64..512} tokens."""
+    from heterogeneous_lora_amd import _lib
+    fake = 0x7F0000000000
+    total, P, d = 196608, 5120, 5120
+    rng = np.random.default_rng(seed)
+    ranks = rng.choice(np.array([8, 16, 32, 64, 128]), size=2000)
+    p = np.arange(1, 2001, dtype=np.float64) ** -0.8
+    p /= p.sum()
+    trace = []
+    for step in range(steps):
+        for _ in range(int(rng.poisson(24))):
+            a = int(rng.choice(2000, p=p))
+            trace.append((step, a, int(ranks[a]), int(rng.integers(16, 257)), int(rng.integers(64, 513))))
+
+    def run(split_frac):
+        if split_frac is None:
+            kv = _lib.Pool(fake, total, P, "f16", seed)
+            ap = kv
+        else:
+            na = int(total * split_frac)
+            ap = _lib.Pool(fake, na, P, "f16", seed, ordered=True)
+            kv = _lib.Pool(fake, total - na, P, "f16", seed)
+        res = _lib.Residency(ap, [d] * 4, [d] * 4)
+        sch = _lib.Scheduler(kv, res, 2, 16384, 1024)
+        out = dict(tokens=0, prefill_tokens=0, decode_tokens=0, finished=0, aborted_pool_full=0,
+                   adapter_fetches=0, adapter_evictions=0, running_sum=0, fetch_bytes=0)
+        at = 0
+        for step in range(steps):
+            while at < len(trace) and trace[at][0] == step:
+                _, a, r, pl, mx = trace[at]
+                sch.submit(at, a, r, pl, mx)
+                at += 1
+            b = sch.step()
+            out["tokens"] += b["n_tokens"]
+            out["prefill_tokens"] += int(b["seg_offsets"][-1])
+            out["decode_tokens"] += b["token_adapter"].size
+            out["finished"] += b["finished"].size
+            out["aborted_pool_full"] += int((b["abort_reason"] == _lib.ABORT_POOL_FULL).sum())
+            out["adapter_fetches"] += b["fetch"].size
+            out["adapter_evictions"] += b["evicted"].size
+            out["fetch_bytes"] += int(sum(int(ranks[a]) * 8 * P * 2 for a in b["fetch"]))
+            out["running_sum"] += b["n_running"]
+        out["mean_running"] = round(out.pop("running_sum") / steps, 1)
+        out["waiting_at_end"] = b["n_waiting"]
+        sch.destroy()
+        res.destroy()
+        kv.destroy()
+        if ap is not kv:
+            ap.destroy()
+        return out
+
+    rows = {"unified": run(None)}
+    for f in fractions:
+        rows[f"split adapters {int(f * 100)}%"] = run(f)
+    return {"steps": steps, "requests": len(trace), "pool_pages": total, "results": rows}
 
 
 def roofline_of(kernels, workload, kernel=None):
@@ -460,6 +533,12 @@ def main():
                     help="decode_7b only: skip the prefill_sgmv sub-record")
     ap.add_argument("--pct-steps", type=int, default=64,
                     help="extra steps, every launch timed, for the p10/p50/p90 kernel durations")
+    ap.add_argument("--variant", default="paged", choices=["paged", "gathered", "split"],
+                    help="paged: slora_apply on the unified pool; gathered: slora_apply_gathered "
+                         "(adapters copied out and padded, then a padded batched GEMM); split: "
+                         "slora_apply with the adapters alone in an ordered pool")
+    ap.add_argument("--capacity-ablation", action="store_true",
+                    help="only the host simulation of unified against split pools (no GPU)")
     ap.add_argument("--overlap-steps", type=int, default=64,
                     help="steps timed while a side-stream adapter fetch runs (0: skip)")
     ap.add_argument("--event-every", type=int, default=4,
@@ -484,6 +563,9 @@ def main():
     if args.calib_copy:
         calib_copy(args.calib_copy, 20)
         return
+    if args.capacity_ablation:
+        print(json.dumps(capacity_ablation(args.steps)), flush=True)
+        return
 
     import torch
     import workloads
@@ -497,7 +579,8 @@ def main():
     dinfo = device_info()
     log(f"[bench] device: {dinfo}")
     main_run = run_workload(wl, policy, args.instances, args.steps, args.warmup, args.event_every,
-                            args.pct_steps, dev, overlap_steps=args.overlap_steps)
+                            args.pct_steps, dev, overlap_steps=args.overlap_steps if args.variant == "paged" else 0,
+                            variant=args.variant)
     roofline = roofline_of(main_run["kernels"], wl.name)
     copy_ref = copy_reference(dev)
     roofline["copy_gbps"] = copy_ref["gbps"]
@@ -508,7 +591,7 @@ def main():
     fetch["frac_of_h2d"] = round(fetch["gbps"] / h2d["gbps"], 4)
 
     prefill = None
-    if args.config == "decode_7b" and not args.no_prefill:
+    if args.config == "decode_7b" and not args.no_prefill and args.variant == "paged":
         pw = workloads.make("prefill_sgmv")
         pr = run_workload(pw, 0, 2, max(10, min(args.steps, 40)), max(2, min(args.warmup, 5)),
                           args.event_every, min(args.pct_steps, 16), dev)
@@ -536,6 +619,7 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.n_tokens, "projections": len(wl.projections),
                    "shape": [[p.d_in, p.d_out] for p in wl.projections],
                    "active_adapters": main_run["active"], "policy": args.policy,
+                   "variant": args.variant,
                    "instances_rotated": args.instances, "accumulate": "f32",
                    "page_elems": wl.page_elems, "pool_pages": wl.n_pages},
         "roofline": roofline,

@@ -104,6 +104,9 @@ def load(path: str = LIB_PATH):
         "slora_expand": ([P, P, P, P, P, _c_i64, P], I),
         "slora_apply": ([P, P, P, P, P, _c_i64, P], I),
         "slora_apply_noalloc": ([P, P, P, P, P], I),
+        "slora_gathered_workspace_size": ([P, P, P], I),
+        "slora_apply_gathered": ([P, P, P, P, P, _c_i64, P], I),
+        "slora_pool_create_ordered": ([P, _c_i64, I, I, P], I),
         "slora_plan_inspect": ([P, P, P, P, I, P], I),
         "slora_timing_enable": ([I], I),
         "slora_workspace_status": ([P, P, P], I),
@@ -152,11 +155,16 @@ def abi_version() -> int:
 class Pool:
     """Owner of one slora_pool handle over caller-owned device memory."""
 
-    def __init__(self, dev_ptr: int, n_pages: int, page_elems: int, dtype: str, seed: int):
+    def __init__(self, dev_ptr: int, n_pages: int, page_elems: int, dtype: str, seed: int,
+                 ordered: bool = False):
         self._lib = load()
         h = ctypes.c_void_p()
-        _check(self._lib.slora_pool_create(ctypes.c_void_p(dev_ptr), n_pages, page_elems,
-                                           DTYPES[dtype], seed, ctypes.byref(h)), "pool_create")
+        if ordered:  # pages handed out in ascending order (no shuffle)
+            _check(self._lib.slora_pool_create_ordered(ctypes.c_void_p(dev_ptr), n_pages, page_elems,
+                                                       DTYPES[dtype], ctypes.byref(h)), "pool_create_ordered")
+        else:
+            _check(self._lib.slora_pool_create(ctypes.c_void_p(dev_ptr), n_pages, page_elems,
+                                               DTYPES[dtype], seed, ctypes.byref(h)), "pool_create")
         self.handle = h
         self.n_pages, self.page_elems, self.dtype = n_pages, page_elems, dtype
 
@@ -379,15 +387,29 @@ def apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
                               _vp(ws), ws_bytes, _vp(stream)), "apply")
 
 
+def gathered_workspace_size(call: Call) -> int:
+    n = _c_i64()
+    _check(load().slora_gathered_workspace_size(ctypes.byref(call.lora), ctypes.byref(call.routing),
+                                                ctypes.byref(n)), "gathered_workspace_size")
+    return n.value
+
+
+def apply_gathered(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
+    _check(load().slora_apply_gathered(ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(x),
+                                       _vp(y), _vp(ws), ws_bytes, _vp(stream)), "apply_gathered")
+
+
 def apply_noalloc(call: Call, x: int, y: int, stream: int):
     _check(load().slora_apply_noalloc(ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(x),
                                       _vp(y), _vp(stream)), "apply_noalloc")
 
 
-def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
-    """slora_apply with its arguments converted once: returns a no-argument callable for
-    callers that repeat the same call (same buffers, new contents) many times."""
-    f = load().slora_apply
+def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int,
+               gathered: bool = False):
+    """slora_apply (or slora_apply_gathered) with its arguments converted once: returns a
+    no-argument callable for callers that repeat the same call (same buffers, new
+    contents) many times."""
+    f = load().slora_apply_gathered if gathered else load().slora_apply
     args = (ctypes.byref(call.lora), ctypes.byref(call.routing), _vp(x), _vp(y), _vp(ws),
             _c_i64(ws_bytes), _vp(stream))
 
@@ -400,7 +422,7 @@ def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int):
     return run
 
 
-KERNELS = ["mbgmv_shrink", "mbgmv_expand", "sgmv_shrink", "sgmv_expand", "mbgmv_fused"]
+KERNELS = ["mbgmv_shrink", "mbgmv_expand", "sgmv_shrink", "sgmv_expand", "mbgmv_fused", "gather"]
 
 
 def timing_enable(on: bool):

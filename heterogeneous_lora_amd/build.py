@@ -23,7 +23,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HOST_SRCS = ["pool.cpp", "plan.cpp", "api.cpp", "sched.cpp"]
-DEVICE_SRCS = ["mbgmv.hip", "sgmv.hip", "fetch.hip", "noalloc.hip"]
+DEVICE_SRCS = ["mbgmv.hip", "sgmv.hip", "fetch.hip", "noalloc.hip", "gather.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}", "-D__HIP_PLATFORM_AMD__=1"]

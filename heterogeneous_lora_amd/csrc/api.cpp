@@ -394,6 +394,137 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
 
 }  // namespace
 
+namespace {
+
+// ---------------------------------------------------------------- gathered baseline
+// A synthetic call over the rank-padded copies: adapter q of the copy is request q.
+struct Gathered {
+  std::vector<int64_t> base;
+  std::vector<int32_t> rank, seg_off, seg_ad;
+  std::vector<float> scale;
+  std::vector<GatherReq> reqs;
+  slora_lora L{};
+  slora_routing R{};
+  int32_t r_pad = 0;
+  int64_t copy_pages = 0;
+  int64_t pages_off = 0, pt_off = 0, sg_off = 0, total = 0;  // workspace layout
+};
+thread_local Gathered t_gathered;
+
+int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+// Validates the call like slora_apply, then lays out requests, copies and workspace.
+int gathered_build(const slora_lora* L, const slora_routing* R, Gathered* g) {
+  PlanView pv;
+  const int64_t bytes = plan_bytes(L, R, &t_scratch, &pv);  // the same validation
+  if (bytes < 0) return (int)bytes;
+  const int32_t cA = (L->d_in + L->page_elems - 1) / L->page_elems;
+  const int32_t cB = (L->d_out + L->page_elems - 1) / L->page_elems;
+  g->base.clear();
+  g->rank.clear();
+  g->scale.clear();
+  g->reqs.clear();
+  g->seg_off.assign(1, 0);
+  g->seg_ad.clear();
+  g->r_pad = 0;
+  auto add = [&](int32_t a, int32_t len) {  // one synthetic segment of len tokens
+    const bool lora = a >= 0 && L->rank[a] > 0;
+    g->seg_ad.push_back(lora ? (int32_t)g->reqs.size() : -1);
+    g->seg_off.push_back(g->seg_off.back() + len);
+    if (lora) {
+      g->reqs.push_back(GatherReq{(int32_t)L->base[a], L->rank[a]});
+      g->scale.push_back(L->scale[a]);
+      g->r_pad = std::max(g->r_pad, L->rank[a]);
+    }
+  };
+  const int32_t S = R->n_segments;
+  for (int32_t s = 0; s < S; ++s) add(R->seg_adapter[s], R->seg_offsets[s + 1] - R->seg_offsets[s]);
+  const int32_t seg_end = S > 0 ? R->seg_offsets[S] : 0;
+  for (int32_t t = seg_end; t < R->n_tokens; ++t) add(R->token_adapter[t - seg_end], 1);
+  const int32_t n_req = (int32_t)g->reqs.size();
+  const int32_t r_pad = std::max(g->r_pad, 1);
+  g->copy_pages = (int64_t)n_req * r_pad * (cA + cB);
+  if (g->copy_pages > INT32_MAX)
+    return fail(SLORA_E_INVALID, "gathered: %lld copy pages", (long long)g->copy_pages);
+  for (int32_t q = 0; q < n_req; ++q) {
+    g->base.push_back((int64_t)q * r_pad * (cA + cB));
+    g->rank.push_back(r_pad);
+  }
+  g->L = *L;
+  g->L.n_pages = std::max<int64_t>(g->copy_pages, 1);
+  g->L.page_table_len = g->copy_pages;
+  g->L.n_adapters = n_req;
+  g->L.base = g->base.data();
+  g->L.rank = g->rank.data();
+  g->L.scale = g->scale.data();
+  g->L.r_max = r_pad;
+  g->R.n_tokens = R->n_tokens;
+  g->R.n_segments = (int32_t)g->seg_ad.size();
+  g->R.seg_offsets = g->seg_off.data();
+  g->R.seg_adapter = g->seg_ad.data();
+  g->R.token_adapter = nullptr;
+  g->R.policy = SLORA_POLICY_SGMV;
+  g->pages_off = 0;
+  g->pt_off = align256(g->copy_pages * L->page_elems * 2);
+  g->sg_off = g->pt_off + align256(g->copy_pages * 4);
+  g->total = g->sg_off + ws_layout(&g->L, &g->R).total;
+  return SLORA_OK;
+}
+
+int run_gathered(const slora_lora* L, const slora_routing* R, const void* x, void* y, void* ws,
+                 int64_t ws_bytes, void* stream) {
+  clear_error();
+  Gathered& g = t_gathered;
+  int rc = gathered_build(L, R, &g);
+  if (rc) return rc;
+  if (!x || !y || misaligned(x, 16) || misaligned(y, 16))
+    return fail(SLORA_E_INVALID, "x / y must be 16-byte aligned device pointers");
+  if (!ws || misaligned(ws, 256)) return fail(SLORA_E_INVALID, "ws must be 256-byte aligned");
+  if (ws_bytes < g.total)
+    return fail(SLORA_E_INVALID, "workspace of %lld bytes is smaller than the %lld needed",
+                (long long)ws_bytes, (long long)g.total);
+  if (g.reqs.empty()) return SLORA_OK;
+  uint8_t* wsb = (uint8_t*)ws;
+  g.L.pool = wsb + g.pages_off;
+  g.L.page_table = (const int32_t*)(wsb + g.pt_off);
+  PlanView pv;
+  const int64_t plan = plan_bytes(&g.L, &g.R, &t_scratch, &pv);
+  if (plan < 0) return (int)plan;
+  const int64_t req_bytes = align256((int64_t)g.reqs.size() * (int64_t)sizeof(GatherReq));
+
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipStream_t s = (hipStream_t)stream;
+  SlotRef slot;
+  rc = acquire_slot((size_t)(req_bytes + plan), s, true, &slot);
+  if (rc) return rc;
+  uint8_t* host = (uint8_t*)slot.host();
+  memcpy(host, g.reqs.data(), g.reqs.size() * sizeof(GatherReq));
+  plan_write(&g.L, &g.R, &t_scratch, host + req_bytes, &pv);
+  Geom src;
+  src.pool = (const uint16_t*)L->pool;
+  src.n_pages = L->n_pages;
+  src.P = L->page_elems;
+  src.dtype = L->dtype;
+  src.d_in = L->d_in;
+  src.d_out = L->d_out;
+  src.cA = (L->d_in + src.P - 1) / src.P;
+  src.cB = (L->d_out + src.P - 1) / src.P;
+  src.pt = L->page_table;
+  src.r_max = L->r_max;
+  const hipError_t e = timed_launch(SLORA_K_GATHER, s, [&](const LaunchEvents& le) {
+    return launch_gather(src, (const GatherReq*)host, (int32_t)g.reqs.size(), std::max(g.r_pad, 1),
+                         wsb + g.pages_off, (int32_t*)(wsb + g.pt_off), s, le);
+  });
+  if (e != hipSuccess) rc = hip_fail(e, "gather launch");
+  if (!rc)
+    rc = launch_plan(&g.L, &g.R, pv, x, nullptr, nullptr, y, wsb + g.sg_off, ws_bytes - g.sg_off,
+                     ws_layout(&g.L, &g.R), s, kApply, slot.ring);
+  const int rc2 = release_slot(slot, s, rc == SLORA_OK);
+  return rc ? rc : rc2;
+}
+
+}  // namespace
+
 namespace slora {
 int apply_shared(const slora_lora* L, const slora_routing* R, const void* x, void* y, void* ws,
                  int64_t ws_bytes, void* stream) {
@@ -583,6 +714,22 @@ int slora_workspace_size(const slora_lora* lora, const slora_routing* routing, i
 
 int slora_workspace_status(void* ws, void* stream, int32_t* status) {
   return slora::guarded(__func__, [&] { return impl_slora_workspace_status(ws, stream, status); });
+}
+
+int slora_gathered_workspace_size(const slora_lora* lora, const slora_routing* routing, int64_t* bytes) {
+  return slora::guarded(__func__, [&] {
+    clear_error();
+    if (!bytes) return fail(SLORA_E_INVALID, "gathered_workspace_size: bytes is NULL");
+    const int rc = gathered_build(lora, routing, &t_gathered);
+    if (rc) return rc;
+    *bytes = t_gathered.total;
+    return SLORA_OK;
+  });
+}
+
+int slora_apply_gathered(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
+                         void* ws, int64_t ws_bytes, void* stream) {
+  return slora::guarded(__func__, [&] { return run_gathered(lora, routing, x, y, ws, ws_bytes, stream); });
 }
 
 int slora_set_wait_limit(int32_t polls) {

@@ -184,6 +184,15 @@ hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* t
                               const float* vpart, int32_t v_stride, int64_t split_stride, void* y,
                               hipStream_t s, const LaunchEvents& ev = LaunchEvents());
 
+// Ablation baseline: copy each request's adapter out of the pool into contiguous,
+// rank-padded memory (gather.hip). One entry per request.
+struct GatherReq {
+  int32_t pt_base;  // the adapter's first page-table entry
+  int32_t rank;     // its rank (rows at or past it are zero in the copy)
+};
+hipError_t launch_gather(const Geom& g, const GatherReq* reqs, int32_t n_req, int32_t r_pad,
+                         void* dst, int32_t* dst_pt, hipStream_t s, const LaunchEvents& ev);
+
 constexpr int kFetchMaxPages = 240;
 struct FetchArgs {
   const uint16_t* src;  // device-visible pointer to pinned host rows (rows x L)

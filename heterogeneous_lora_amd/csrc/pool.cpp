@@ -121,7 +121,7 @@ const char* slora_last_error(void) { return t_error.c_str(); }
 int slora_abi_version(void) { return SLORA_ABI_VERSION; }
 
 static int impl_slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
-                      uint64_t shuffle_seed, slora_pool** out) {
+                      uint64_t shuffle_seed, bool ordered, slora_pool** out) {
   clear_error();
   if (!out) return fail(SLORA_E_INVALID, "pool_create: out is NULL");
   *out = nullptr;
@@ -144,10 +144,14 @@ static int impl_slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page
   p->owner.assign((size_t)n_pages, kFree);
   p->free_list.resize((size_t)n_pages);
   for (int64_t i = 0; i < n_pages; ++i) p->free_list[(size_t)i] = (int32_t)i;
-  SplitMix64 rng{shuffle_seed};
-  for (int64_t i = n_pages - 1; i > 0; --i) {  // Fisher-Yates
-    int64_t j = (int64_t)rng.below((uint64_t)i + 1);
-    std::swap(p->free_list[(size_t)i], p->free_list[(size_t)j]);
+  if (ordered) {  // a stack popped from the back: pages are handed out in ascending order
+    std::reverse(p->free_list.begin(), p->free_list.end());
+  } else {
+    SplitMix64 rng{shuffle_seed};
+    for (int64_t i = n_pages - 1; i > 0; --i) {  // Fisher-Yates
+      int64_t j = (int64_t)rng.below((uint64_t)i + 1);
+      std::swap(p->free_list[(size_t)i], p->free_list[(size_t)j]);
+    }
   }
   *out = p;
   return SLORA_OK;
@@ -421,7 +425,12 @@ extern "C" {
 
 int slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
                       uint64_t shuffle_seed, slora_pool** out) {
-  return slora::guarded(__func__, [&] { return impl_slora_pool_create(dev_pages, n_pages, page_elems, dtype, shuffle_seed, out); });
+  return slora::guarded(__func__, [&] { return impl_slora_pool_create(dev_pages, n_pages, page_elems, dtype, shuffle_seed, false, out); });
+}
+
+int slora_pool_create_ordered(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
+                              slora_pool** out) {
+  return slora::guarded(__func__, [&] { return impl_slora_pool_create(dev_pages, n_pages, page_elems, dtype, 0, true, out); });
 }
 
 int slora_pool_destroy(slora_pool* pool) {

@@ -286,12 +286,15 @@ int do_step(slora_sched* s) {
     const bool lora = s->res && q.adapter >= 0 && q.rank > 0;
     if (lora) {
       // room for the adapter (unless resident) and the prompt's KV together, from free
-      // pages and evictions of other unpinned adapters; then pin the adapter
+      // pages and evictions of other unpinned adapters; then pin the adapter. With the
+      // adapters in a pool of their own, the two needs are met by their own pools.
       auto it = s->res->resident.find(q.adapter);
       const int64_t a_need = it == s->res->resident.end() ? need_pages(s->res, q.rank) : 0;
+      const bool unified = s->res->pool == s->pool;
+      if (!unified && pool_free(s->pool) < kv_need) break;
       std::vector<int32_t> victims;
       bool enough = false;
-      rc = plan_evictions(s->res, a_need + kv_need, &victims, &enough, q.adapter);
+      rc = plan_evictions(s->res, unified ? a_need + kv_need : a_need, &victims, &enough, q.adapter);
       if (rc) return rc;
       if (!enough) break;
       for (int32_t v : victims) {
@@ -425,7 +428,6 @@ int slora_sched_create(slora_pool* pool, slora_residency* res, const slora_sched
     if (!out) return fail(SLORA_E_INVALID, "sched_create: out is NULL");
     *out = nullptr;
     if (!pool || !cfg) return fail(SLORA_E_INVALID, "sched_create: pool / config is NULL");
-    if (res && res->pool != pool) return fail(SLORA_E_INVALID, "sched_create: residency of another pool");
     if (cfg->kv_pages_per_token < 1 || cfg->max_running < 1 || cfg->max_batch_tokens < cfg->max_running)
       return fail(SLORA_E_INVALID, "sched_create: kv_pages_per_token, max_running >= 1 and "
                   "max_batch_tokens >= max_running required");

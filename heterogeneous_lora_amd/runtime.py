@@ -56,16 +56,25 @@ class PagedLoRA:
 
     def __init__(self, wl, device: str = "cuda", adapters: Optional[List[int]] = None,
                  fill_kv: bool = True, sentinel: bool = True, pool_seed: Optional[int] = None,
-                 store: Optional[HostStore] = None):
+                 store: Optional[HostStore] = None, ordered: bool = False,
+                 n_pages: Optional[int] = None):
+        """ordered: a pool of its own for the adapters, pages handed out in order (each
+        adapter contiguous), no KV pages in it (the split-memory ablation); n_pages then
+        defaults to the adapters' pages plus the workload's spare."""
         self.wl = wl
         self.device = torch.device(device)
         P = wl.page_elems
-        self.pool_t = torch.empty(wl.n_pages * P, dtype=torch.int16, device=self.device)
+        self.adapters = [int(a) for a in (wl.active_adapters() if adapters is None else adapters)]
+        if ordered:
+            fill_kv = False
+            if n_pages is None:
+                n_pages = sum(wl.adapter_pages(a) for a in self.adapters) + 64
+        self.n_pages = wl.n_pages if n_pages is None else n_pages
+        self.pool_t = torch.empty(self.n_pages * P, dtype=torch.int16, device=self.device)
         if sentinel:
             self.pool_t.fill_(SENTINEL_I16[wl.dtype])
-        self.pool = _lib.Pool(self.pool_t.data_ptr(), wl.n_pages, P, wl.dtype,
-                              wl.pool_seed if pool_seed is None else pool_seed)
-        self.adapters = [int(a) for a in (wl.active_adapters() if adapters is None else adapters)]
+        self.pool = _lib.Pool(self.pool_t.data_ptr(), self.n_pages, P, wl.dtype,
+                              wl.pool_seed if pool_seed is None else pool_seed, ordered=ordered)
         d_in = [p.d_in for p in wl.projections]
         d_out = [p.d_out for p in wl.projections]
         for a in self.adapters:
@@ -124,7 +133,7 @@ class PagedLoRA:
     def call(self, proj: int, policy: int = _lib.POLICY_AUTO, wl=None) -> _lib.Call:
         wl = wl or self.wl
         p = wl.projections[proj]
-        return _lib.Call(pool_ptr=self.pool_t.data_ptr(), n_pages=wl.n_pages,
+        return _lib.Call(pool_ptr=self.pool_t.data_ptr(), n_pages=self.n_pages,
                          page_elems=wl.page_elems, dtype=wl.dtype, d_in=p.d_in, d_out=p.d_out,
                          page_table_ptr=self.pt_dev[proj].data_ptr(),
                          page_table_len=self.pt_len[proj], base=self.base[proj], rank=wl.ranks,
@@ -141,17 +150,25 @@ class PagedLoRA:
         """Device workspace for calls like `call` (zero-filled once, as the library requires)."""
         return torch.zeros(_lib.workspace_size(call), dtype=torch.uint8, device=self.device)
 
+    def gathered_workspace(self, call: _lib.Call) -> torch.Tensor:
+        return torch.zeros(_lib.gathered_workspace_size(call), dtype=torch.uint8, device=self.device)
+
+    def apply_gathered(self, call, x, y, ws, stream=None):
+        s = stream or torch.cuda.current_stream(self.device)
+        _lib.apply_gathered(call, x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), s.cuda_stream)
+
     def apply(self, call: _lib.Call, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
               stream: Optional[torch.cuda.Stream] = None):
         s = stream or torch.cuda.current_stream(self.device)
         _lib.apply(call, x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), s.cuda_stream)
 
     def bind_apply(self, call: _lib.Call, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
-                   stream: Optional[torch.cuda.Stream] = None):
-        """apply() with its arguments marshalled once (a callable with no arguments)."""
+                   stream: Optional[torch.cuda.Stream] = None, gathered: bool = False):
+        """apply() (or apply_gathered()) with its arguments marshalled once (a callable
+        with no arguments)."""
         s = stream or torch.cuda.current_stream(self.device)
         return _lib.bind_apply(call, x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(),
-                               s.cuda_stream)
+                               s.cuda_stream, gathered=gathered)
 
     def shrink(self, call, x, v, ws, stream=None):
         s = stream or torch.cuda.current_stream(self.device)

@@ -97,6 +97,15 @@ int slora_abi_version(void);
 int slora_pool_create(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
                       uint64_t shuffle_seed, slora_pool** out);
 
+/* A pool whose free list is not shuffled: pages are handed out in ascending id order
+ * (so pages allocated together, such as one adapter's, are consecutive) and freed pages
+ * are reused last-freed first. For the ablation of the unified pool (the S-LoRA
+ * overview, section "S-LoRA的性能评估": S-LoRA without unified memory keeps adapters
+ * and the KV cache in separate memory): an adapter-only pool of this kind stores each
+ * adapter contiguously, and KV pages come from a second pool. */
+int slora_pool_create_ordered(void* dev_pages, int64_t n_pages, int32_t page_elems, int32_t dtype,
+                              slora_pool** out);
+
 /* Destroy the handle (waits for this pool's fetches to finish). NULL is a no-op. */
 int slora_pool_destroy(slora_pool* pool);
 
@@ -251,8 +260,10 @@ typedef struct {
   int64_t free_pages;             /* of the pool, after the step */
 } slora_sched_batch;
 
-/* A scheduler over `pool`; `res` (may be NULL: adapters are then the caller's
- * business) manages the adapters requests use. */
+/* A scheduler over `pool`, which holds the KV pages; `res` (may be NULL: adapters are
+ * then the caller's business) manages the adapters requests use, in its own pool: the
+ * same pool (unified paging: adapters and KV compete for one free list) or another one
+ * (adapters and KV in separate memory). */
 int slora_sched_create(slora_pool* pool, slora_residency* res, const slora_sched_config* cfg,
                        slora_sched** out);
 /* Frees the running requests' KV pages and unpins their adapters, then the scheduler. */
@@ -334,6 +345,21 @@ int slora_expand(const slora_lora* lora, const slora_routing* routing, const flo
 int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
                 void* ws, int64_t ws_bytes, void* stream);
 
+/* Ablation baseline "S-LoRA with conventional batched matmul" (the S-LoRA overview,
+ * section "S-LoRA的性能评估", comparison of S-LoRA variants): the same function as
+ * slora_apply, computed the conventional way. Every request (a segment, or a decode
+ * token on its own) gets a contiguous copy of its adapter, gathered out of the pool and
+ * padded with zero rows to the largest rank of the batch, and one padded batched GEMM
+ * (the MFMA segment kernels over the copies, every adapter at the padded rank) produces
+ * y. Results agree with slora_apply within rounding. The workspace (caller-owned, size
+ * from slora_gathered_workspace_size, zero-filled once) holds the copies: n_requests x
+ * r_pad x (ceil(d_in/P) + ceil(d_out/P)) pages. The routing's policy is ignored; no
+ * launch of this path waits across workgroups, so it has no workspace status. */
+int slora_gathered_workspace_size(const slora_lora* lora, const slora_routing* routing,
+                                  int64_t* bytes);
+int slora_apply_gathered(const slora_lora* lora, const slora_routing* routing, const void* x,
+                         void* y, void* ws, int64_t ws_bytes, void* stream);
+
 /* slora_apply for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments minus
  * the workspace, same kernels, same results bit for bit. The workspace is a static
@@ -381,7 +407,8 @@ int slora_set_wait_limit(int32_t polls);
 #define SLORA_K_SGMV_SHRINK 2
 #define SLORA_K_SGMV_EXPAND 3
 #define SLORA_K_MBGMV_FUSED 4
-#define SLORA_K_COUNT 5
+#define SLORA_K_GATHER 5 /* slora_apply_gathered's copy of the adapters out of the pool */
+#define SLORA_K_COUNT 6
 int slora_timing_enable(int32_t on);
 
 /* Waits for the recorded events, then writes per kernel id the number of timed

@@ -366,3 +366,45 @@ def test_sched_with_residency_pins_fetches_and_evicts():
     assert res.info()["pinned"] == 0
     res.destroy()
     pool.destroy()
+
+
+def test_ordered_pool_hands_out_pages_in_order():
+    """The pool of the split-memory ablation: no shuffle, so one adapter's pages are
+    consecutive, and a scheduler can take KV pages from one pool while its residency
+    manager keeps adapters in another."""
+    apool = _lib.Pool(FAKE_DEV, 1000, P, "f16", 0, ordered=True)
+    apool.alloc_adapter(3, 4, D_IN, D_OUT)
+    apool.alloc_adapter(1, 2, D_IN, D_OUT)
+    for proj in (0, 1):
+        pt, base, rank = apool.page_table(proj, 4)
+        per_row = -(-D_IN[proj] // P) + -(-D_OUT[proj] // P)
+        for a in (1, 3):  # each adapter's pages of a projection are consecutive
+            seg = pt[base[a]:base[a] + rank[a] * per_row]
+            assert np.array_equal(seg, np.arange(seg[0], seg[0] + seg.size))
+    own = apool.owners()
+    assert (own[:32] == 3).all() and (own[32:48] == 1).all() and (own[48:] == -1).all()
+    kv = _pool(400)
+    res = _lib.Residency(apool, D_IN, D_OUT)
+    sched = _lib.Scheduler(kv, res, 2, 128, 8)
+    sched.submit(0, 7, 8, 50, 3)
+    b = sched.step()
+    assert list(b["fetch"]) == [7] and res.pins(7) == 1
+    assert kv.n_free() == 400 - 100 and (kv.owners() == -2).sum() == 100
+    assert (apool.owners() == 7).sum() == pages_of(8)
+    sched.destroy()
+    res.destroy()
+    kv.destroy()
+    apool.destroy()
+
+
+def test_capacity_ablation_runs_on_the_host():
+    """bench.py's unified-against-split simulation: both configurations serve the same
+    trace; every token served is a prefill or a decode token."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    d = bench.capacity_ablation(steps=40, fractions=(0.5,))
+    assert set(d["results"]) == {"unified", "split adapters 50%"}
+    for r in d["results"].values():
+        assert r["tokens"] == r["prefill_tokens"] + r["decode_tokens"] > 0
