@@ -308,6 +308,8 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     store = runtime.HostStore(wl, active)
     host_io = [(wl.x(p), wl.y0(p)) for p in range(n_proj)]
     insts, fetch_ms = [], []
+    _lib.timing_enable(True)  # the fetch kernels of the instances' setup are timed too
+    _lib.timing_read_all()
     for i in range(n_inst):
         inst = runtime.PagedLoRA(wl, device=dev, store=store, pool_seed=wl.pool_seed + i,
                                  ordered=variant == "split")
@@ -319,6 +321,9 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
         insts.append((inst, calls, io, ws))
         log(f"[bench] instance {i} ready (fetch {inst.fetch_ms:.2f} ms)")
     del host_io
+    _lib.timing_enable(False)
+    fnames, fms_all = _lib.timing_read_all()
+    fetch_kernel_ms = [m for n, m in zip(fnames, fms_all) if n == "fetch"]
     fetch_bytes = sum(int(wl.ranks[a]) * (p.d_in + p.d_out) * 2 for a in active for p in wl.projections)
 
     stream = torch.cuda.current_stream(dev)
@@ -369,9 +374,9 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
         torch.cuda.synchronize()
         side.wait_stream(stream)
         f0.record(side)
-        for a in tgt.adapters:
-            at, bb = tgt.store.ptrs(a, n_proj)
-            tgt.pool.fetch_async(a, at, bb, side.cuda_stream, None)
+        rows = [tgt.store.ptrs(a, n_proj) for a in tgt.adapters]
+        tgt.pool.fetch_many_async(tgt.adapters, [r[0] for r in rows], [r[1] for r in rows],
+                                  side.cuda_stream, None)
         f1.record(side)
         _lib.timing_enable(True)
         t2 = time.perf_counter()
@@ -434,7 +439,10 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
                step_kernel_us=round(kern_total_s * 1e6, 2),
                step_algorithmic_gbps=round(step_bytes / kern_total_s / 1e9, 1),
                fetch={"bytes": fetch_bytes, "ms": round(fms, 3),
-                      "gbps": round(fetch_bytes / (fms * 1e-3) / 1e9, 2)},
+                      "gbps": round(fetch_bytes / (fms * 1e-3) / 1e9, 2),
+                      "kernel_ms": round(float(np.median(fetch_kernel_ms)), 3) if fetch_kernel_ms else None,
+                      "kernel_gbps": round(fetch_bytes / (float(np.median(fetch_kernel_ms)) * 1e-3) / 1e9, 2)
+                      if fetch_kernel_ms else None},
                active=len(active), workspace_status="clean", fetch_overlap=overlap)
     for inst, *_ in insts:
         inst.close()
@@ -589,6 +597,8 @@ def main():
     h2d = h2d_reference(dev, fetch["bytes"])
     fetch["h2d_copy_engine_gbps"] = h2d["gbps"]
     fetch["frac_of_h2d"] = round(fetch["gbps"] / h2d["gbps"], 4)
+    if fetch.get("kernel_gbps"):
+        fetch["kernel_frac_of_h2d"] = round(fetch["kernel_gbps"] / h2d["gbps"], 4)
 
     prefill = None
     if args.config == "decode_7b" and not args.no_prefill and args.variant == "paged":

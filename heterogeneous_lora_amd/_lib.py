@@ -99,6 +99,7 @@ def load(path: str = LIB_PATH):
         "slora_pool_page_table": ([P, I, I, P, _c_i64, P, P, P], I),
         "slora_pool_owners": ([P, P], I),
         "slora_fetch_async": ([P, I, P, P, P, P], I),
+        "slora_fetch_many_async": ([P, I, P, P, P, P, P], I),
         "slora_workspace_size": ([P, P, P], I),
         "slora_shrink": ([P, P, P, P, P, _c_i64, P], I),
         "slora_expand": ([P, P, P, P, P, _c_i64, P], I),
@@ -229,6 +230,32 @@ class Pool:
         _check(self._lib.slora_fetch_async(self.handle, adapter_id, at, b, ctypes.c_void_p(stream),
                                            ctypes.c_void_p(event) if event else None),
                "fetch_async")
+
+    def fetch_many_async(self, adapter_ids: Sequence[int], host_at: Sequence[Sequence[int]],
+                         host_b: Sequence[Sequence[int]], stream: int, event: Optional[int]):
+        """fetch_async for several adapters in one launch; host_at[i] / host_b[i] are
+        adapter_ids[i]'s per-projection row pointers."""
+        n = len(adapter_ids)
+        if len(host_at) != n or len(host_b) != n:
+            raise ValueError("fetch_many_async: one pointer list per adapter")
+        ids = np.ascontiguousarray(adapter_ids, dtype=np.int32)
+
+        def table(lists):
+            # the per-adapter pointer arrays as rows of one uint64 block, and an array of
+            # the rows' addresses (both kept alive by the caller's references)
+            width = max([len(x) for x in lists] + [1])
+            block = np.zeros((max(n, 1), width), np.uint64)
+            for i, x in enumerate(lists):
+                block[i, :len(x)] = x
+            rows = block.ctypes.data + np.arange(max(n, 1), dtype=np.uint64) * np.uint64(width * 8)
+            return block, np.ascontiguousarray(rows, dtype=np.uint64)
+
+        blk_at, at = table(host_at)
+        blk_b, b = table(host_b)
+        _check(self._lib.slora_fetch_many_async(self.handle, n, _p(ids), _p(at), _p(b),
+                                                ctypes.c_void_p(stream),
+                                                ctypes.c_void_p(event) if event else None),
+               "fetch_many_async")
 
 
 class Residency:
@@ -422,7 +449,8 @@ def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int,
     return run
 
 
-KERNELS = ["mbgmv_shrink", "mbgmv_expand", "sgmv_shrink", "sgmv_expand", "mbgmv_fused", "gather"]
+KERNELS = ["mbgmv_shrink", "mbgmv_expand", "sgmv_shrink", "sgmv_expand", "mbgmv_fused", "gather",
+           "fetch"]
 
 
 def timing_enable(on: bool):

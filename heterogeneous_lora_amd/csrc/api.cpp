@@ -526,6 +526,14 @@ int run_gathered(const slora_lora* L, const slora_routing* R, const void* x, voi
 }  // namespace
 
 namespace slora {
+hipError_t timed_fetch(const FetchPage* pages, int64_t n, uint16_t* pool, int32_t page_elems,
+                       hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return timed_launch(SLORA_K_FETCH, s, [&](const LaunchEvents& le) {
+    return launch_fetch(pages, n, pool, page_elems, s, le);
+  });
+}
+
 int apply_shared(const slora_lora* L, const slora_routing* R, const void* x, void* y, void* ws,
                  int64_t ws_bytes, void* stream) {
   return run(L, R, x, nullptr, nullptr, y, ws, ws_bytes, stream, kApply, true);

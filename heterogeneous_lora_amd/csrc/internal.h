@@ -193,18 +193,18 @@ struct GatherReq {
 hipError_t launch_gather(const Geom& g, const GatherReq* reqs, int32_t n_req, int32_t r_pad,
                          void* dst, int32_t* dst_pt, hipStream_t s, const LaunchEvents& ev);
 
-constexpr int kFetchMaxPages = 240;
-struct FetchArgs {
-  const uint16_t* src;  // device-visible pointer to pinned host rows (rows x L)
-  uint16_t* pool;
-  int32_t P;
-  int32_t L;            // row length
-  int32_t chunks;       // pages per row
-  int32_t e0;           // first (row * chunks + chunk) entry of this launch
-  int32_t n;            // pages in this launch
-  int32_t pad;
-  int32_t pages[kFetchMaxPages];
+// Adapter fetch (fetch.hip): one workgroup per destination page, the page list read by
+// the kernel from pinned host memory. 16 bytes per page.
+struct FetchPage {
+  const uint16_t* src;  // device-visible address of the page's first element in pinned host rows
+  int32_t page;         // destination pool page
+  int32_t len;          // elements to copy (<= page_elems; the rest of the page is left as is)
 };
-hipError_t launch_fetch(const FetchArgs& a, hipStream_t s);
+static_assert(sizeof(FetchPage) == 16, "FetchPage layout");
+hipError_t launch_fetch(const FetchPage* pages, int64_t n, uint16_t* pool, int32_t page_elems,
+                        hipStream_t s, const LaunchEvents& ev = LaunchEvents());
+// launch_fetch, timed as SLORA_K_FETCH while kernel timing is on (api.cpp).
+hipError_t timed_fetch(const FetchPage* pages, int64_t n, uint16_t* pool, int32_t page_elems,
+                       hipStream_t s);
 
 }  // namespace slora

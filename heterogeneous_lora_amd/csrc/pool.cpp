@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <map>
+#include <memory>
 #include <mutex>
 
 #include "guard.h"
@@ -48,12 +49,19 @@ using namespace slora;
 
 namespace {
 
+// The completion event of one fetch call, shared by the adapters it moved.
+struct FetchMark {
+  hipEvent_t ev = nullptr;
+  ~FetchMark() {
+    if (ev) (void)hipEventDestroy(ev);
+  }
+};
+
 struct AdapterRec {
   int32_t rank = 0;
   std::vector<int32_t> d_in, d_out;
   std::vector<std::vector<int32_t>> pages;  // per projection, page-table order
-  hipEvent_t ev = nullptr;                  // last fetch into this adapter
-  bool fetch_recorded = false;
+  std::shared_ptr<FetchMark> fetch;         // the last fetch into this adapter, if any
 };
 
 // splitmix64: a small seeded generator for the free-list shuffle
@@ -78,6 +86,16 @@ constexpr int32_t kKV = -2;
 
 }  // namespace
 
+// Pinned page lists of fetch launches, reused round-robin; one is refilled only after
+// the launch that read it has finished (its event).
+constexpr int kFetchStages = 4;
+struct FetchStage {
+  slora::FetchPage* host = nullptr;
+  int64_t cap = 0;  // entries
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
 struct slora_pool {
   void* dev = nullptr;
   int64_t n_pages = 0;
@@ -86,6 +104,9 @@ struct slora_pool {
   std::vector<int32_t> free_list;  // stack: pop from the back
   std::vector<int32_t> owner;      // per page: adapter id, kFree or kKV
   std::map<int32_t, AdapterRec> adapters;
+  FetchStage stage[kFetchStages];
+  int stage_next = 0;
+  std::vector<slora::FetchPage> pages_scratch;  // a call's page list before it is staged
 };
 
 namespace slora {
@@ -96,8 +117,8 @@ int pool_adapter_state(const slora_pool* pool, int32_t id, int64_t* pages, bool*
   auto it = pool->adapters.find(id);
   if (it == pool->adapters.end()) return SLORA_OK;
   for (const auto& pg : it->second.pages) *pages += (int64_t)pg.size();
-  if (it->second.ev && it->second.fetch_recorded) {
-    const hipError_t e = hipEventQuery(it->second.ev);
+  if (it->second.fetch) {
+    const hipError_t e = hipEventQuery(it->second.fetch->ev);
     if (e == hipErrorNotReady) *busy = true;
     else if (e != hipSuccess) return hip_fail(e, "hipEventQuery");
   }
@@ -163,13 +184,18 @@ static int impl_slora_pool_destroy(slora_pool* pool) {
   int rc = SLORA_OK;
   for (auto& kv : pool->adapters) {
     AdapterRec& a = kv.second;
-    if (a.ev) {
-      if (a.fetch_recorded) {
-        hipError_t e = hipEventSynchronize(a.ev);
-        if (e != hipSuccess && rc == SLORA_OK) rc = hip_fail(e, "pool_destroy: hipEventSynchronize");
-      }
-      (void)hipEventDestroy(a.ev);
+    if (a.fetch) {
+      hipError_t e = hipEventSynchronize(a.fetch->ev);
+      if (e != hipSuccess && rc == SLORA_OK) rc = hip_fail(e, "pool_destroy: hipEventSynchronize");
     }
+  }
+  for (FetchStage& st : pool->stage) {
+    if (st.pending) {
+      hipError_t e = hipEventSynchronize(st.ev);
+      if (e != hipSuccess && rc == SLORA_OK) rc = hip_fail(e, "pool_destroy: hipEventSynchronize");
+    }
+    if (st.ev) (void)hipEventDestroy(st.ev);
+    if (st.host) (void)hipHostFree(st.host);
   }
   delete pool;
   return rc;
@@ -274,14 +300,13 @@ static int impl_slora_pool_free_adapter(slora_pool* pool, int32_t adapter_id) {
   if (it == pool->adapters.end())
     return fail(SLORA_E_STATE, "free_adapter: adapter %d is not resident", adapter_id);
   AdapterRec& a = it->second;
-  if (a.ev && a.fetch_recorded) {
-    hipError_t e = hipEventQuery(a.ev);
+  if (a.fetch) {
+    hipError_t e = hipEventQuery(a.fetch->ev);
     if (e == hipErrorNotReady)
       return fail(SLORA_E_STATE, "free_adapter: a fetch into adapter %d is still in flight",
                   adapter_id);
     if (e != hipSuccess) return hip_fail(e, "free_adapter: hipEventQuery");
   }
-  if (a.ev) (void)hipEventDestroy(a.ev);
   for (auto& pg : a.pages)
     for (int32_t id : pg) {
       pool->owner[(size_t)id] = kFree;
@@ -338,8 +363,9 @@ static int impl_slora_pool_owners(const slora_pool* pool, int32_t* owner) {
 }
 
 // Host rows are read by the fetch kernel straight from pinned memory over PCIe
-// (zero-copy), one workgroup per destination page, so one launch covers up to
-// kFetchMaxPages pages with no staging buffer and no per-page DMA call.
+// (zero-copy), one workgroup per destination page; the page list is staged in pinned
+// memory too, so one launch covers every page of a call with no device staging buffer
+// and no per-page DMA call.
 static int device_view(const void* host, const void** dev, const char* what) {
   hipPointerAttribute_t attr;
   memset(&attr, 0, sizeof attr);
@@ -358,63 +384,136 @@ static int device_view(const void* host, const void** dev, const char* what) {
   return SLORA_OK;
 }
 
-static int impl_slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
-                      const void* const* host_B, void* side_stream, void* done_event) {
+// Appends the pages of one matrix (rows x L, row-major at the device-visible src) whose
+// page-table entries start at pg[first]: row k, chunk c -> pg[first + k * chunks + c].
+static void add_pages(std::vector<FetchPage>* out, const uint16_t* src, int32_t rows, int32_t L,
+                      int32_t P, const std::vector<int32_t>& pg, int32_t first) {
+  const int32_t chunks = (L + P - 1) / P;
+  for (int32_t k = 0; k < rows; ++k)
+    for (int32_t c = 0; c < chunks; ++c)
+      out->push_back(FetchPage{src + (int64_t)k * L + (int64_t)c * P,
+                               pg[(size_t)(first + k * chunks + c)], std::min(P, L - c * P)});
+}
+
+static int impl_fetch_many(slora_pool* pool, int32_t n, const int32_t* ids,
+                           const void* const* const* host_AT, const void* const* const* host_B,
+                           void* side_stream, void* done_event) {
   clear_error();
   if (!pool) return fail(SLORA_E_INVALID, "fetch: pool is NULL");
-  auto it = pool->adapters.find(adapter_id);
-  if (it == pool->adapters.end())
-    return fail(SLORA_E_STATE, "fetch: adapter %d is not resident", adapter_id);
-  AdapterRec& a = it->second;
-  const int32_t n_proj = (int32_t)a.pages.size();
-  if (a.rank > 0 && (!host_AT || !host_B)) return fail(SLORA_E_INVALID, "fetch: host arrays are NULL");
+  if (n < 0 || (n > 0 && !ids)) return fail(SLORA_E_INVALID, "fetch: %d adapters, ids %p", n, (const void*)ids);
   hipStream_t s = (hipStream_t)side_stream;
-  // validate every source before the first launch
-  std::vector<const void*> srcA((size_t)n_proj), srcB((size_t)n_proj);
-  for (int32_t p = 0; p < n_proj && a.rank > 0; ++p) {
-    if (!host_AT[p] || !host_B[p]) return fail(SLORA_E_INVALID, "fetch: projection %d source NULL", p);
-    if ((reinterpret_cast<uintptr_t>(host_AT[p]) | reinterpret_cast<uintptr_t>(host_B[p])) & 15)
-      return fail(SLORA_E_INVALID, "fetch: host rows must be 16-byte aligned");
-    int rc = device_view(host_AT[p], &srcA[(size_t)p], "host_AT");
-    if (rc) return rc;
-    rc = device_view(host_B[p], &srcB[(size_t)p], "host_B");
-    if (rc) return rc;
-  }
-  if (!a.ev) {
-    hipError_t e = hipEventCreateWithFlags(&a.ev, hipEventDisableTiming);
-    if (e != hipSuccess) { a.ev = nullptr; return hip_fail(e, "fetch: hipEventCreate"); }
-  }
-  for (int32_t p = 0; p < n_proj && a.rank > 0; ++p) {
-    const int32_t cA = (a.d_in[(size_t)p] + pool->P - 1) / pool->P;
-    const int32_t cB = (a.d_out[(size_t)p] + pool->P - 1) / pool->P;
-    const std::vector<int32_t>& pg = a.pages[(size_t)p];
-    for (int half = 0; half < 2; ++half) {
-      FetchArgs fa;
-      memset(&fa, 0, sizeof fa);
-      fa.src = (const uint16_t*)(half == 0 ? srcA[(size_t)p] : srcB[(size_t)p]);
-      fa.pool = (uint16_t*)pool->dev;
-      fa.P = pool->P;
-      fa.L = half == 0 ? a.d_in[(size_t)p] : a.d_out[(size_t)p];
-      fa.chunks = half == 0 ? cA : cB;
-      const int32_t first = half == 0 ? 0 : a.rank * cA;
-      const int32_t total = a.rank * fa.chunks;
-      for (int32_t e0 = 0; e0 < total; e0 += kFetchMaxPages) {
-        fa.e0 = e0;
-        fa.n = std::min(kFetchMaxPages, total - e0);
-        for (int32_t q = 0; q < fa.n; ++q) fa.pages[q] = pg[(size_t)(first + e0 + q)];
-        hipError_t e = launch_fetch(fa, s);
-        if (e != hipSuccess) return hip_fail(e, "fetch: kernel launch");
+  // every adapter and source checked, and the whole page list built, before anything launches
+  for (int32_t i = 0; i < n; ++i)
+    if (pool->adapters.find(ids[i]) == pool->adapters.end())
+      return fail(SLORA_E_STATE, "fetch: adapter %d is not resident", ids[i]);
+  // Device views of this call's sources: the first row pointer in an allocation is looked
+  // up, the others in the same allocation follow from its range (one query per buffer
+  // instead of one per matrix); a matrix that would run past its allocation is refused.
+  struct View {
+    uintptr_t h0, h1, d0;
+  };
+  std::vector<View> views;
+  auto view = [&](const void* host, int64_t bytes, const void** dev, const char* what) -> int {
+    const uintptr_t h = reinterpret_cast<uintptr_t>(host);
+    for (const View& v : views)
+      if (h >= v.h0 && h < v.h1) {
+        if (h + (uintptr_t)bytes > v.h1)
+          return fail(SLORA_E_INVALID, "fetch: %s rows run past the end of their allocation", what);
+        *dev = reinterpret_cast<const void*>(v.d0 + (h - v.h0));
+        return SLORA_OK;
       }
+    const int rc = device_view(host, dev, what);
+    if (rc) return rc;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)host) == hipSuccess && size > 0 &&
+        reinterpret_cast<uintptr_t>(base) <= h && h < reinterpret_cast<uintptr_t>(base) + size) {
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(base);
+      if (h + (uintptr_t)bytes > b0 + size)
+        return fail(SLORA_E_INVALID, "fetch: %s rows run past the end of their allocation", what);
+      views.push_back(View{b0, b0 + size, reinterpret_cast<uintptr_t>(*dev) - (h - b0)});
+    } else {
+      (void)hipGetLastError();
+    }
+    return SLORA_OK;
+  };
+  std::vector<FetchPage>& d = pool->pages_scratch;
+  d.clear();
+  for (int32_t i = 0; i < n; ++i) {
+    const AdapterRec& a = pool->adapters.find(ids[i])->second;
+    if (a.rank <= 0) continue;
+    if (!host_AT || !host_B || !host_AT[i] || !host_B[i])
+      return fail(SLORA_E_INVALID, "fetch: host arrays of adapter %d are NULL", ids[i]);
+    for (size_t p = 0; p < a.pages.size(); ++p) {
+      const void* at = host_AT[i][p];
+      const void* b = host_B[i][p];
+      if (!at || !b) return fail(SLORA_E_INVALID, "fetch: projection %zu source NULL", p);
+      if ((reinterpret_cast<uintptr_t>(at) | reinterpret_cast<uintptr_t>(b)) & 15)
+        return fail(SLORA_E_INVALID, "fetch: host rows must be 16-byte aligned");
+      const void *dat = nullptr, *db = nullptr;
+      int rc = view(at, (int64_t)a.rank * a.d_in[p] * 2, &dat, "host_AT");
+      if (rc) return rc;
+      rc = view(b, (int64_t)a.rank * a.d_out[p] * 2, &db, "host_B");
+      if (rc) return rc;
+      const int32_t cA = (a.d_in[p] + pool->P - 1) / pool->P;
+      add_pages(&d, (const uint16_t*)dat, a.rank, a.d_in[p], pool->P, a.pages[p], 0);
+      add_pages(&d, (const uint16_t*)db, a.rank, a.d_out[p], pool->P, a.pages[p], a.rank * cA);
     }
   }
-  hipError_t e = hipEventRecord(a.ev, s);
-  if (e != hipSuccess) return hip_fail(e, "fetch: hipEventRecord");
-  a.fetch_recorded = true;
+  if (!d.empty()) {
+    FetchStage& st = pool->stage[pool->stage_next];
+    if (st.pending) {  // the launch that last read this list must be done
+      const hipError_t e = hipEventSynchronize(st.ev);
+      if (e != hipSuccess) return hip_fail(e, "fetch: hipEventSynchronize");
+      st.pending = false;
+    }
+    if (st.cap < (int64_t)d.size()) {
+      if (st.host) (void)hipHostFree(st.host);
+      st.host = nullptr;
+      st.cap = 0;
+      const int64_t cap = std::max<int64_t>((int64_t)d.size(), 4096);
+      void* h = nullptr;
+      const hipError_t e = hipHostMalloc(&h, (size_t)cap * sizeof(FetchPage), hipHostMallocDefault);
+      if (e != hipSuccess) return hip_fail(e, "fetch: hipHostMalloc");
+      st.host = (FetchPage*)h;
+      st.cap = cap;
+    }
+    if (!st.ev) {
+      const hipError_t e = hipEventCreateWithFlags(&st.ev, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        st.ev = nullptr;
+        return hip_fail(e, "fetch: hipEventCreate");
+      }
+    }
+    memcpy(st.host, d.data(), d.size() * sizeof(FetchPage));
+    hipError_t e = timed_fetch(st.host, (int64_t)d.size(), (uint16_t*)pool->dev, pool->P, s);
+    if (e != hipSuccess) return hip_fail(e, "fetch: kernel launch");
+    e = hipEventRecord(st.ev, s);
+    if (e != hipSuccess) return hip_fail(e, "fetch: hipEventRecord");
+    st.pending = true;
+    pool->stage_next = (pool->stage_next + 1) % kFetchStages;
+  }
+  if (n > 0) {  // one fetch-in-flight marker for every adapter of the call
+    auto mark = std::make_shared<FetchMark>();
+    hipError_t e = hipEventCreateWithFlags(&mark->ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      mark->ev = nullptr;
+      return hip_fail(e, "fetch: hipEventCreate");
+    }
+    e = hipEventRecord(mark->ev, s);
+    if (e != hipSuccess) return hip_fail(e, "fetch: hipEventRecord");
+    for (int32_t i = 0; i < n; ++i) pool->adapters.find(ids[i])->second.fetch = mark;
+  }
   if (done_event) {
-    e = hipEventRecord((hipEvent_t)done_event, s);
+    hipError_t e = hipEventRecord((hipEvent_t)done_event, s);
     if (e != hipSuccess) return hip_fail(e, "fetch: hipEventRecord(done)");
   }
   return SLORA_OK;
+}
+
+static int impl_slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
+                                  const void* const* host_B, void* side_stream, void* done_event) {
+  return impl_fetch_many(pool, 1, &adapter_id, &host_AT, &host_B, side_stream, done_event);
 }
 
 }  // extern "C"
@@ -482,6 +581,12 @@ int slora_pool_owners(const slora_pool* pool, int32_t* owner) {
 int slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
                       const void* const* host_B, void* side_stream, void* done_event) {
   return slora::guarded(__func__, [&] { return impl_slora_fetch_async(pool, adapter_id, host_AT, host_B, side_stream, done_event); });
+}
+
+int slora_fetch_many_async(slora_pool* pool, int32_t n, const int32_t* adapter_ids,
+                           const void* const* const* host_AT, const void* const* const* host_B,
+                           void* side_stream, void* done_event) {
+  return slora::guarded(__func__, [&] { return impl_fetch_many(pool, n, adapter_ids, host_AT, host_B, side_stream, done_event); });
 }
 
 }  // extern "C"

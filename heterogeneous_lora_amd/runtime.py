@@ -121,10 +121,9 @@ class PagedLoRA:
         done.record(side)  # creates the event so its handle can be passed down
         n_proj = len(self.wl.projections)
         todo = self.adapters if adapters is None else adapters
-        for i, a in enumerate(todo):
-            at, b = self.store.ptrs(a, n_proj)
-            last = i == len(todo) - 1
-            self.pool.fetch_async(a, at, b, side.cuda_stream, done.cuda_event if last else None)
+        rows = [self.store.ptrs(a, n_proj) for a in todo]
+        self.pool.fetch_many_async(todo, [r[0] for r in rows], [r[1] for r in rows],
+                                   side.cuda_stream, done.cuda_event)
         torch.cuda.current_stream(self.device).wait_event(done)
         self._fetch_done = done
         done.synchronize()
@@ -228,10 +227,11 @@ class ServingLoop:
         if b["fetch"].size:
             done = torch.cuda.Event()
             self.side.wait_stream(self.stream)
-            for a in b["fetch"]:
-                at, bb = self.store.ptrs(int(a), 1)
-                self.pool.fetch_async(int(a), at, bb, self.side.cuda_stream, None)
-                self.fetch_bytes += int(self.wl.ranks[int(a)]) * (self.d_in + self.d_out) * 2
+            ids = [int(a) for a in b["fetch"]]
+            rows = [self.store.ptrs(a, 1) for a in ids]
+            self.pool.fetch_many_async(ids, [r[0] for r in rows], [r[1] for r in rows],
+                                       self.side.cuda_stream, None)
+            self.fetch_bytes += sum(int(self.wl.ranks[a]) * (self.d_in + self.d_out) * 2 for a in ids)
             done.record(self.side)
             self.stream.wait_event(done)
         if b["n_tokens"] == 0:

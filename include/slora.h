@@ -165,6 +165,18 @@ int slora_pool_owners(const slora_pool* pool, int32_t* owner);
 int slora_fetch_async(slora_pool* pool, int32_t adapter_id, const void* const* host_AT,
                       const void* const* host_B, void* side_stream, void* done_event);
 
+/* slora_fetch_async for n adapters at once (one kernel launch moves every page): adapter
+ * adapter_ids[i] takes its rows from host_AT[i][p] / host_B[i][p], laid out as for
+ * slora_fetch_async. The S-LoRA serving loop fetches the adapters a batch needs together
+ * (review, "Proposed method"). All-or-nothing: every id and source is checked before
+ * anything is launched (SLORA_E_STATE for an id that is not resident). An id may appear
+ * twice (its pages are written twice with the same bytes). The page list is staged in
+ * library-owned pinned memory; a fifth call in a row may wait on the host for the
+ * first one's launch to finish before it reuses that list. */
+int slora_fetch_many_async(slora_pool* pool, int32_t n, const int32_t* adapter_ids,
+                           const void* const* const* host_AT, const void* const* const* host_B,
+                           void* side_stream, void* done_event);
+
 /* ------------------------------------------------------------------ adapter residency
  * All adapters stay in host memory; those running requests use are fetched to the pool
  * on demand (review, abstract and "Proposed method"), and when the active set outgrows
@@ -408,7 +420,8 @@ int slora_set_wait_limit(int32_t polls);
 #define SLORA_K_SGMV_EXPAND 3
 #define SLORA_K_MBGMV_FUSED 4
 #define SLORA_K_GATHER 5 /* slora_apply_gathered's copy of the adapters out of the pool */
-#define SLORA_K_COUNT 6
+#define SLORA_K_FETCH 6  /* slora_fetch_async / slora_fetch_many_async's copy into the pool */
+#define SLORA_K_COUNT 7
 int slora_timing_enable(int32_t on);
 
 /* Waits for the recorded events, then writes per kernel id the number of timed

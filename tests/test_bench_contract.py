@@ -47,7 +47,8 @@ def test_bench_prints_one_json_line():
     assert d["workspace_status"] == "clean"
     k = d["kernels"][r["kernel"]]
     assert k["p10_us"] <= k["p50_us"] <= k["p90_us"] and k["pct_launches"] >= 8
-    assert d["fetch"]["h2d_copy_engine_gbps"] > 0
+    f = d["fetch"]
+    assert f["h2d_copy_engine_gbps"] > 0 and f["kernel_gbps"] > 0 and 0 < f["kernel_ms"] <= f["ms"]
     assert d["device"]["compute_units"] > 0
     pf = d["prefill"]
     assert pf["workload"] == "prefill_sgmv" and pf["value"] > 0 and pf["workspace_status"] == "clean"

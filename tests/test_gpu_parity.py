@@ -290,6 +290,62 @@ def test_fetch_byte_exact_and_sentinels(rt):
     inst.close()
 
 
+def _check_pages(rt, wl, inst, adapters):
+    """Every page of `adapters` holds exactly its host rows with the sentinel past the row
+    end; returns the set of pages checked."""
+    pool = inst.pool_t.cpu().numpy().view(np.uint16).reshape(inst.n_pages, wl.page_elems)
+    P = wl.page_elems
+    sentinel = rt.SENTINEL_I16[wl.dtype]
+    seen = set()
+    for pi, p in enumerate(wl.projections):
+        cA, cB = -(-p.d_in // P), -(-p.d_out // P)
+        pt = inst.pt_dev[pi].cpu().numpy()
+        for a in adapters:
+            at, b = wl.adapter(a, pi)
+            r = at.shape[0]
+            base = int(inst.base[pi][a])
+            for k in range(r):
+                for half, rows, c, L in ((0, at, cA, p.d_in), (1, b, cB, p.d_out)):
+                    for ch in range(c):
+                        page = pt[base + (0 if half == 0 else r * cA) + k * c + ch]
+                        n = min(P, L - ch * P)
+                        assert np.array_equal(pool[page, :n], rows[k, ch * P:ch * P + n]), (a, pi, k, half, ch)
+                        assert np.all(pool[page, n:] == sentinel)
+                        seen.add(int(page))
+    return seen
+
+
+def test_fetch_many_rounds_and_duplicates(rt):
+    """Batched fetches in more rounds than the library keeps pinned page lists (each list is
+    refilled only after its launch finished): every round leaves exactly its adapters' pages
+    written, an id given twice included, the other pages untouched."""
+    wl = workloads.random_small(213, d_in=1000, d_out=264, page_elems=256, n_tokens=30,
+                                n_segments=0, rank_choices=(3, 8, 16), n_adapters=7, n_pages=600)
+    say("[gpu] fetch_many rounds")
+    inst = rt.PagedLoRA(wl, adapters=list(range(wl.n_adapters)))
+    side = torch.cuda.Stream()
+    rng = np.random.default_rng(3)
+    sentinel = rt.SENTINEL_I16[wl.dtype]
+    for rnd in range(6):
+        torch.cuda.synchronize()
+        inst.pool_t.fill_(sentinel)
+        torch.cuda.synchronize()
+        pick = [int(a) for a in rng.choice(wl.n_adapters, size=3, replace=False)]
+        ids = pick + [pick[0]]
+        rows = [inst.store.ptrs(a, 1) for a in ids]
+        done = torch.cuda.Event()
+        side.wait_stream(torch.cuda.current_stream())
+        inst.pool.fetch_many_async(ids, [r[0] for r in rows], [r[1] for r in rows],
+                                   side.cuda_stream, done.cuda_event)
+        done.synchronize()
+        seen = _check_pages(rt, wl, inst, pick)
+        pool = inst.pool_t.cpu().numpy().view(np.uint16).reshape(inst.n_pages, wl.page_elems)
+        rest = np.ones(inst.n_pages, bool)
+        rest[list(seen)] = False
+        assert np.all(pool[rest] == sentinel), rnd
+    inst.close()
+
+
 @pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
 def test_probe_codes_bit_exact(rt, policy):
     """Integer-coded adapters: one-hot x reads back every A^T code exactly through shrink

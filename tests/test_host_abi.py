@@ -119,6 +119,17 @@ def test_pool_errors_all_or_nothing():
         with pytest.raises(_lib.SloraError) as e:
             pool.alloc_adapter(9, bad.get("rank", 4), bad["d_in"], bad["d_out"])
         assert e.value.code == _lib.E_INVALID
+    # a batched fetch checks every id before anything reaches a device
+    with pytest.raises(_lib.SloraError) as e:
+        pool.fetch_many_async([0, 7], [[0x1000], [0x1000]], [[0x1000], [0x1000]], 0, None)
+    assert e.value.code == _lib.E_STATE and "adapter 7" in str(e.value)
+    with pytest.raises(_lib.SloraError) as e:
+        pool.fetch_many_async([0], [[0]], [[0]], 0, None)
+    assert e.value.code == _lib.E_INVALID
+    with pytest.raises(_lib.SloraError) as e:
+        pool.fetch_many_async([0], [[0x1008]], [[0x1000]], 0, None)  # misaligned rows
+    assert e.value.code == _lib.E_INVALID
+    pool.fetch_many_async([], [], [], 0, None)  # nothing to move, nothing launched
     pool.destroy()
     with pytest.raises(_lib.SloraError):
         _lib.Pool(FAKE_DEV + 8, 10, 64, "f16", 0)  # misaligned
