@@ -88,18 +88,19 @@ constexpr int32_t kSgMinSplit = 3;
 // 16-row blocks of rank rows the shrink template for ranks up to max_rank holds.
 constexpr int shrink_nb(int max_rank) { return max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8; }
 
+// One (tile, k-range) with NB 16-row blocks; slab holds 2 x 16 NB x kSegs vectors.
 template <int DT, int NB>
-__global__ __launch_bounds__(64 * kWaves, shrink_waves(NB)) void sgmv_shrink_kernel(
-    Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t kc,
-    const uint16_t* __restrict__ x, float* __restrict__ vpart, int32_t v_stride,
-    int64_t split_stride) {
+__device__ __forceinline__ void shrink_tile(const Geom& g, const SgTile& tl,
+                                            const int32_t* __restrict__ tok, int32_t kc,
+                                            const uint16_t* __restrict__ x,
+                                            float* __restrict__ vpart, int32_t v_stride,
+                                            int64_t split_stride, uint4* slab_mem) {
   constexpr int kRows = 16 * NB;
   constexpr int kLoads = kRows * kSegs / (64 * kWaves);  // slab vectors per thread
   static_assert(kLoads >= 1 && kRows * kSegs == kLoads * 64 * kWaves, "slab split");
-  __shared__ uint4 slab[2][kRows * kSegs];
+  uint4 (*slab)[kRows * kSegs] = reinterpret_cast<uint4 (*)[kRows * kSegs]>(slab_mem);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
-  const SgTile tl = tiles[blockIdx.x];
   const int ks = blockIdx.y;
   const int kb = ks * kc, ke = min(g.d_in, kb + kc);
   const int r = tl.rank;
@@ -201,26 +202,46 @@ __global__ __launch_bounds__(64 * kWaves, shrink_waves(NB)) void sgmv_shrink_ker
   }
 }
 
+// NBM: the widest template of the launch (its registers, LDS and occupancy); each tile
+// runs the narrowest one that holds its rank, so a low-rank tile loads, stages and
+// multiplies only its own rows (the branch is uniform per workgroup and taken once).
+template <int DT, int NBM>
+__global__ __launch_bounds__(64 * kWaves, shrink_waves(NBM)) void sgmv_shrink_kernel(
+    Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t kc,
+    const uint16_t* __restrict__ x, float* __restrict__ vpart, int32_t v_stride,
+    int64_t split_stride) {
+  __shared__ uint4 slab[2 * 16 * NBM * kSegs];
+  const SgTile tl = tiles[blockIdx.x];
+  const int nb = shrink_nb(tl.rank);
+  if (NBM >= 8 && nb == 8) shrink_tile<DT, NBM >= 8 ? 8 : NBM>(g, tl, tok, kc, x, vpart, v_stride, split_stride, slab);
+  else if (NBM >= 4 && nb == 4) shrink_tile<DT, NBM >= 4 ? 4 : NBM>(g, tl, tok, kc, x, vpart, v_stride, split_stride, slab);
+  else if (NBM >= 2 && nb == 2) shrink_tile<DT, NBM >= 2 ? 2 : NBM>(g, tl, tok, kc, x, vpart, v_stride, split_stride, slab);
+  else shrink_tile<DT, 1>(g, tl, tok, kc, x, vpart, v_stride, split_stride, slab);
+}
+
 // ------------------------------------------------------------------ expand
 constexpr int kCols = 128;                 // output columns of one pass (32 per wave)
 constexpr int kSubPasses = 8;              // passes per workgroup (1024 columns)
 constexpr int kBPitch = kCols + 4;         // B chunk row pitch in elements (bank spread)
 constexpr int kChunkRows = kStep;          // B rows staged per chunk
 
-// KB: 32-row chunks of the rank (rank <= 32 * KB).
+// LDS of the expand template for KB 32-row chunks: v rows, then the B stages.
+constexpr int expand_vs_elems(int kb) { return kTileRows * (kb * kStep + 8); }
+constexpr int expand_bbufs(int kb) { return kb <= 2 ? 2 : 1; }  // two B stages: one barrier per pass
+constexpr int expand_bs_elems(int kb) { return expand_bbufs(kb) * kb * kChunkRows * kBPitch; }
+
+// One (tile, column block) with KB 32-row chunks of the rank (rank <= 32 * KB).
 template <int DT, int KB>
-__global__ __launch_bounds__(64 * kWaves, expand_waves(KB)) void sgmv_expand_kernel(
-    Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t ksplit,
-    const float* __restrict__ vpart, int32_t v_stride, int64_t split_stride,
-    uint16_t* __restrict__ y) {
+__device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
+                                            const int32_t* __restrict__ tok, int32_t ksplit,
+                                            const float* __restrict__ vpart, int32_t v_stride,
+                                            int64_t split_stride, uint16_t* __restrict__ y,
+                                            uint16_t* vs, uint16_t* bs) {
   constexpr int kRp = KB * kStep;     // padded rank
   constexpr int kVPitch = kRp + 8;    // v row pitch in elements
-  __shared__ uint16_t vs[kTileRows * kVPitch];
-  constexpr int kBBufs = KB <= 2 ? 2 : 1;  // two B stages: one barrier per pass
-  __shared__ uint16_t bs[kBBufs * KB * kChunkRows * kBPitch];
+  constexpr int kBBufs = expand_bbufs(KB);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
-  const SgTile tl = tiles[blockIdx.x];
   const int r = tl.rank;
   const int col_begin = blockIdx.y * (kSubPasses * kCols);
   const int n_pass = min(kSubPasses, (g.d_out - col_begin + kCols - 1) / kCols);
@@ -399,6 +420,29 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KB)) void sgmv_expand_ker
       if (pass + 2 < n_pass) load_y0(ya, pass + 2);
       run_pass(pass + 1, yb);
     }
+  }
+}
+
+// KBM: the widest template of the launch (its registers, LDS and occupancy); each tile
+// runs the narrowest one that holds its rank (uniform per workgroup, taken once). The
+// widest launch (ranks above 64) keeps its one body: next to the narrower bodies its
+// register spills grew (36 -> 44 bytes per lane) and mixed_13b's expand slowed
+// (60.2 -> 62.6 us), while the narrower launches gained (prefill_sgmv expand 90.5 ->
+// 88.1 us, shrink 50.9 -> 49.8 us; mlp_asym shrink 121.8 -> 117.5 us).
+template <int DT, int KBM>
+__global__ __launch_bounds__(64 * kWaves, expand_waves(KBM)) void sgmv_expand_kernel(
+    Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t ksplit,
+    const float* __restrict__ vpart, int32_t v_stride, int64_t split_stride,
+    uint16_t* __restrict__ y) {
+  constexpr int kBsMax = expand_bs_elems(KBM) > expand_bs_elems(2) ? expand_bs_elems(KBM) : expand_bs_elems(2);
+  __shared__ uint16_t vs[expand_vs_elems(KBM)];
+  __shared__ uint16_t bs[KBM >= 2 ? kBsMax : expand_bs_elems(1)];
+  const SgTile tl = tiles[blockIdx.x];
+  if constexpr (KBM >= 4) {
+    expand_tile<DT, 4>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
+  } else {
+    if (KBM >= 2 && tl.rank > 32) expand_tile<DT, KBM>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
+    else expand_tile<DT, 1>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
   }
 }
 
