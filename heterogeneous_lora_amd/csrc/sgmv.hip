@@ -40,6 +40,8 @@ using namespace dev;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kStep = 32;          // k per MFMA
@@ -55,6 +57,18 @@ __device__ __forceinline__ f32x4 mfma(const uint4& a, const uint4& b, f32x4 c) {
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x16_{f16,bf16}: the same layout with 4 consecutive k per lane (at
+// (l / 16) * 4), for operands of 16 rows of k (ranks up to 16).
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(const uint2& a, const uint2& b, f32x4 c) {
+  if constexpr (DT == SLORA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
 // Token of row m of a tile, or -1 past its end.
@@ -230,16 +244,19 @@ constexpr int expand_vs_elems(int kb) { return kTileRows * (kb * kStep + 8); }
 constexpr int expand_bbufs(int kb) { return kb <= 2 ? 2 : 1; }  // two B stages: one barrier per pass
 constexpr int expand_bs_elems(int kb) { return expand_bbufs(kb) * kb * kChunkRows * kBPitch; }
 
-// One (tile, column block) with KB 32-row chunks of the rank (rank <= 32 * KB).
-template <int DT, int KB>
+// One (tile, column block) with KB chunks of KS rows of the rank (rank <= KS * KB); KS is
+// the k of one product: 32 (16x16x32), or 16 (16x16x16) for ranks up to 16.
+template <int DT, int KB, int KS = kStep>
 __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
                                             const int32_t* __restrict__ tok, int32_t ksplit,
                                             const float* __restrict__ vpart, int32_t v_stride,
                                             int64_t split_stride, uint16_t* __restrict__ y,
                                             uint16_t* vs, uint16_t* bs) {
-  constexpr int kRp = KB * kStep;     // padded rank
+  static_assert(KS == 16 || KS == 32, "k per product");
+  constexpr int kRp = KB * KS;        // padded rank
   constexpr int kVPitch = kRp + 8;    // v row pitch in elements
   constexpr int kBBufs = expand_bbufs(KB);
+  constexpr int kChunk = KS;          // B rows staged per chunk
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
   const int r = tl.rank;
@@ -250,10 +267,11 @@ __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) tk[tb] = tile_token(tl, tok, tb * 16 + li);
 
-  // B staging: thread -> column slot (8 columns) and rows ch * 32 + row0 + 16 i of every
+  // B staging: thread -> column slot (8 columns) and rows ch * KS + row0 + 16 i of every
   // chunk. A pass's rows are loaded in one go, a pass ahead; the page ids of the
   // thread's rows are kept while the pass's columns stay in the same page chunk.
-  constexpr int kSlots = kCols / 8, kRowStep = 64 * kWaves / kSlots, kBLoads = kChunkRows / kRowStep;
+  constexpr int kSlots = kCols / 8, kRowStep = 64 * kWaves / kSlots, kBLoads = kChunk / kRowStep;
+  static_assert(kBLoads >= 1 && kBLoads * kRowStep == kChunk, "B staging split");
   const int slot = tid % kSlots, row0 = tid / kSlots;
   int pid_c = -1;
   int pids[KB][kBLoads];
@@ -267,7 +285,7 @@ __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
       for (int ch = 0; ch < KB; ++ch)
 #pragma unroll
         for (int i = 0; i < kBLoads; ++i) {
-          const int kr = ch * kChunkRows + row0 + i * kRowStep;
+          const int kr = ch * kChunk + row0 + i * kRowStep;
           pids[ch][i] = kr < r ? g.pt[bbase + (int64_t)kr * g.cB] : -1;
         }
       pid_c = bc;
@@ -276,7 +294,7 @@ __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
     for (int ch = 0; ch < KB; ++ch)
 #pragma unroll
       for (int i = 0; i < kBLoads; ++i) {
-        const int kr = ch * kChunkRows + row0 + i * kRowStep;
+        const int kr = ch * kChunk + row0 + i * kRowStep;
         const uint16_t* p = fill_zero();
         if (live && kr < r) {
           const int page = pids[ch][i];
@@ -291,7 +309,7 @@ __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
     for (int ch = 0; ch < KB; ++ch)
 #pragma unroll
       for (int i = 0; i < kBLoads; ++i) {
-        uint2* d = reinterpret_cast<uint2*>(&bs[((buf * KB + ch) * kChunkRows + row0 + i * kRowStep) * kBPitch + slot * 8]);
+        uint2* d = reinterpret_cast<uint2*>(&bs[((buf * KB + ch) * kChunk + row0 + i * kRowStep) * kBPitch + slot * 8]);
         d[0] = make_uint2(b[ch][i].x, b[ch][i].y);
         d[1] = make_uint2(b[ch][i].z, b[ch][i].w);
       }
@@ -364,25 +382,42 @@ __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
     __syncthreads();
 #pragma unroll
     for (int ch = 0; ch < KB; ++ch) {
-      const uint16_t* bsc = bs + (buf * KB + ch) * kChunkRows * kBPitch;
-      // v^T operand: token tb * 16 + li, k = ch * 32 + kg * 8 + [0, 8)
-      uint4 vo[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        vo[tb] = *reinterpret_cast<const uint4*>(&vs[(tb * 16 + li) * kVPitch + ch * kStep + kg * 8]);
+      const uint16_t* bsc = bs + (buf * KB + ch) * kChunk * kBPitch;
+      constexpr int kPer = KS / 4;  // k of one lane's operand
       // B^T operand: output column (h, li) = (li / 4) * 8 + h * 4 + li % 4 of this wave's 32,
-      // k = kg * 8 + [0, 8) of the chunk
+      // k = kg * kPer + [0, kPer) of the chunk; v^T operand: token tb * 16 + li, the same k
+      if constexpr (KS == 32) {
+        uint4 vo[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int colw = wave * 32 + (li >> 2) * 8 + h * 4 + (li & 3);
-        const uint16_t* src = &bsc[(kg * 8) * kBPitch + colw];
-        uint4 bo;
-        bo.x = (uint32_t)src[0 * kBPitch] | ((uint32_t)src[1 * kBPitch] << 16);
-        bo.y = (uint32_t)src[2 * kBPitch] | ((uint32_t)src[3 * kBPitch] << 16);
-        bo.z = (uint32_t)src[4 * kBPitch] | ((uint32_t)src[5 * kBPitch] << 16);
-        bo.w = (uint32_t)src[6 * kBPitch] | ((uint32_t)src[7 * kBPitch] << 16);
+        for (int tb = 0; tb < 4; ++tb)
+          vo[tb] = *reinterpret_cast<const uint4*>(&vs[(tb * 16 + li) * kVPitch + ch * KS + kg * kPer]);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[h][tb] = mfma<DT>(bo, vo[tb], acc[h][tb]);
+        for (int h = 0; h < 2; ++h) {
+          const int colw = wave * 32 + (li >> 2) * 8 + h * 4 + (li & 3);
+          const uint16_t* src = &bsc[(kg * kPer) * kBPitch + colw];
+          uint4 bo;
+          bo.x = (uint32_t)src[0 * kBPitch] | ((uint32_t)src[1 * kBPitch] << 16);
+          bo.y = (uint32_t)src[2 * kBPitch] | ((uint32_t)src[3 * kBPitch] << 16);
+          bo.z = (uint32_t)src[4 * kBPitch] | ((uint32_t)src[5 * kBPitch] << 16);
+          bo.w = (uint32_t)src[6 * kBPitch] | ((uint32_t)src[7 * kBPitch] << 16);
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) acc[h][tb] = mfma<DT>(bo, vo[tb], acc[h][tb]);
+        }
+      } else {
+        uint2 vo[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          vo[tb] = *reinterpret_cast<const uint2*>(&vs[(tb * 16 + li) * kVPitch + ch * KS + kg * kPer]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int colw = wave * 32 + (li >> 2) * 8 + h * 4 + (li & 3);
+          const uint16_t* src = &bsc[(kg * kPer) * kBPitch + colw];
+          uint2 bo;
+          bo.x = (uint32_t)src[0 * kBPitch] | ((uint32_t)src[1 * kBPitch] << 16);
+          bo.y = (uint32_t)src[2 * kBPitch] | ((uint32_t)src[3 * kBPitch] << 16);
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) acc[h][tb] = mfma16<DT>(bo, vo[tb], acc[h][tb]);
+        }
       }
     }
     // lane: token tk[tb], columns col + h * 4 + q
@@ -442,7 +477,8 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KBM)) void sgmv_expand_ke
     expand_tile<DT, 4>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
   } else {
     if (KBM >= 2 && tl.rank > 32) expand_tile<DT, KBM>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
-    else expand_tile<DT, 1>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
+    else if (tl.rank > 16) expand_tile<DT, 1>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
+    else expand_tile<DT, 1, 16>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
   }
 }
 
