@@ -399,11 +399,9 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
                    "fetch_gbps_during_apply": round(fetch_bytes / (f_ms * 1e-3) / 1e9, 2),
                    "steps_inside_fetch": int(min(overlap_steps, f_ms * 1e-3 / max((t3 - t2) / overlap_steps, 1e-9)))}
         log(f"[bench] apply during a side-stream fetch: {json.dumps(overlap)}")
-    # (the gathered variant runs no decode launch that waits, and its workspace has no header)
-    bad = [] if variant == "gathered" else [
-        i for i, (_, _, _, ws) in enumerate(insts) if _lib.workspace_status(ws.data_ptr(), stream.cuda_stream)]
+    bad = [i for i, (_, _, _, ws) in enumerate(insts) if _lib.workspace_status(ws.data_ptr(), stream.cuda_stream)]
     if bad:
-        print(f"bench.py: a decode launch gave up waiting in instance(s) {bad}: results invalid",
+        print(f"bench.py: a fused launch gave up waiting in instance(s) {bad}: results invalid",
               file=sys.stderr)
         sys.exit(3)
 
@@ -430,7 +428,7 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     kern_total_s = float(np.sum(ms)) * 1e-3 / n_timed
     step_bytes = sum(kv["algorithmic_bytes"] * kv["launches"] for kv in kernels.values()) / n_timed
     if variant != "paged":  # the same function: the paged path's algorithmic bytes per step
-        step_bytes = sum(a[f]["bytes"] for a in alg for f in ("mbgmv_fused", "sgmv_shrink", "sgmv_expand"))
+        step_bytes = sum(a[f]["bytes"] for a in alg for f in ("mbgmv_fused", "sgmv_fused"))
     log(f"[bench] kernels: {json.dumps(kernels)}")
     log(f"[bench] all kernels of a step: {kern_total_s * 1e6:.1f} us, "
         f"{step_bytes / kern_total_s / 1e9:.0f} GB/s algorithmic")
@@ -611,7 +609,7 @@ def main():
                    "kernels": pr["kernels"], "step_kernel_us": pr["step_kernel_us"],
                    "step_algorithmic_gbps": pr["step_algorithmic_gbps"],
                    "roofline": {k: roofline_of(pr["kernels"], pw.name, k)
-                                for k in ("sgmv_shrink", "sgmv_expand") if k in pr["kernels"]},
+                                for k in ("sgmv_fused",) if k in pr["kernels"]},
                    "workspace_status": pr["workspace_status"]}
 
     cpu = None

@@ -305,7 +305,7 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
   const float* vr = mode == kApply ? v : v_in;
   hipError_t e = hipSuccess;
   uint32_t tag = 0;
-  if (mode == kApply && pv.n_mb) {
+  if (mode == kApply && (pv.n_mb || pv.n_sg)) {
     // A fresh tag per fused call on this workspace; before a tag could repeat, the
     // workspace past its header is cleared so no stale word can carry it (the header
     // keeps any give-up until slora_workspace_status reads it).
@@ -316,7 +316,7 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
       last = 0;
     }
     tag = ++last;
-    const int rc = order_fused(*ring, s);
+    const int rc = order_fused(*ring, s);  // both families' fused launches wait within a launch
     if (rc) return rc;
   }
   if (pv.n_sg) {
@@ -349,7 +349,17 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
       if (e1 != hipSuccess) return e1;
       return one(hi, pv.n_sg - hi, pv.sg[hi].rank, second);
     };
-    if (mode & kShrink) {
+    if (mode == kApply) {
+      uint32_t* flags = (uint32_t*)(wsb + lay.flg_off);
+      e = timed_launch(SLORA_K_SGMV_FUSED, s, [&](const LaunchEvents& le) {
+        return by_rank(le, [&](int32_t t0, int32_t nt, int32_t mr, const LaunchEvents& l) {
+          return launch_sgmv_fused(g, pv.tok, pv.sg + t0, nt, mr, sp.ksplit, sp.kc, x, vpart,
+                                   v_stride, stride, flags + (int64_t)t0 * sp.ksplit, tag,
+                                   g_spin_limit, err, y, s, l);
+        });
+      });
+      if (e != hipSuccess) return hip_fail(e, "sgmv_fused launch");
+    } else if (mode & kShrink) {
       e = timed_launch(SLORA_K_SGMV_SHRINK, s, [&](const LaunchEvents& le) {
         return by_rank(le, [&](int32_t t0, int32_t nt, int32_t mr, const LaunchEvents& l) {
           return launch_sgmv_shrink(g, pv.tok, pv.sg + t0, nt, mr, sp.ksplit, sp.kc, x, vpart,
@@ -358,7 +368,7 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
       });
       if (e != hipSuccess) return hip_fail(e, "sgmv_shrink launch");
     }
-    if (mode & kExpand) {
+    if (mode == kExpand) {
       e = timed_launch(SLORA_K_SGMV_EXPAND, s, [&](const LaunchEvents& le) {
         return by_rank(le, [&](int32_t t0, int32_t nt, int32_t mr, const LaunchEvents& l) {
           return launch_sgmv_expand(g, pv.tok, pv.sg + t0, nt, mr, sp.ksplit, vpart, v_stride,
@@ -464,10 +474,12 @@ int gathered_build(const slora_lora* L, const slora_routing* R, Gathered* g) {
   g->R.seg_adapter = g->seg_ad.data();
   g->R.token_adapter = nullptr;
   g->R.policy = SLORA_POLICY_SGMV;
-  g->pages_off = 0;
-  g->pt_off = align256(g->copy_pages * L->page_elems * 2);
-  g->sg_off = g->pt_off + align256(g->copy_pages * 4);
-  g->total = g->sg_off + ws_layout(&g->L, &g->R).total;
+  // The apply's own workspace comes first, so its header (the give-up word) is the
+  // header of the caller's workspace; the copies and their page table follow it.
+  g->sg_off = 0;
+  g->pages_off = align256(ws_layout(&g->L, &g->R).total);
+  g->pt_off = g->pages_off + align256(g->copy_pages * L->page_elems * 2);
+  g->total = g->pt_off + align256(g->copy_pages * 4);
   return SLORA_OK;
 }
 
@@ -517,7 +529,7 @@ int run_gathered(const slora_lora* L, const slora_routing* R, const void* x, voi
   });
   if (e != hipSuccess) rc = hip_fail(e, "gather launch");
   if (!rc)
-    rc = launch_plan(&g.L, &g.R, pv, x, nullptr, nullptr, y, wsb + g.sg_off, ws_bytes - g.sg_off,
+    rc = launch_plan(&g.L, &g.R, pv, x, nullptr, nullptr, y, wsb + g.sg_off, g.pages_off - g.sg_off,
                      ws_layout(&g.L, &g.R), s, kApply, slot.ring);
   const int rc2 = release_slot(slot, s, rc == SLORA_OK);
   return rc ? rc : rc2;

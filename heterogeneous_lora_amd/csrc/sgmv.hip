@@ -24,6 +24,17 @@
 //     the matrix cores) is staged in LDS once; the columns are walked in passes of
 //     128 (32 per wave) whose B rows pass through LDS in 32-row chunks, the B^T
 //     operand read out column-wise, while the next pass's y0 is already loading.
+//
+// slora_apply runs both halves in one launch (sgmv_fused_kernel): the first
+// n_tiles * ksplit workgroups are the shrink items, the rest the expand items. A
+// shrink item stores its partial sums at device (agent) scope, waits for its stores,
+// and then stores its flag word (the call's tag); an expand item polls its tile's
+// ksplit flags before it reads the partial sums, also at agent scope, so neither side
+// needs a cache flush. Shrink items precede every expand item in dispatch order and
+// never wait, so every wait ends; the poll is bounded all the same, and a give-up is
+// recorded in the workspace header. One launch instead of two removes the drain of
+// the shrink grid before the expand grid can start. slora_shrink / slora_expand keep
+// the two separate kernels.
 #include <algorithm>
 
 #include <map>
@@ -103,19 +114,20 @@ constexpr int32_t kSgMinSplit = 3;
 constexpr int shrink_nb(int max_rank) { return max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8; }
 
 // One (tile, k-range) with NB 16-row blocks; slab holds 2 x 16 NB x kSegs vectors.
-template <int DT, int NB>
+// kCoherent: the partial sums are stored at agent scope (performed at the device's
+// coherence point), for a reader in the same launch.
+template <int DT, int NB, bool kCoherent = false>
 __device__ __forceinline__ void shrink_tile(const Geom& g, const SgTile& tl,
                                             const int32_t* __restrict__ tok, int32_t kc,
                                             const uint16_t* __restrict__ x,
                                             float* __restrict__ vpart, int32_t v_stride,
-                                            int64_t split_stride, uint4* slab_mem) {
+                                            int64_t split_stride, int ks, uint4* slab_mem) {
   constexpr int kRows = 16 * NB;
   constexpr int kLoads = kRows * kSegs / (64 * kWaves);  // slab vectors per thread
   static_assert(kLoads >= 1 && kRows * kSegs == kLoads * 64 * kWaves, "slab split");
   uint4 (*slab)[kRows * kSegs] = reinterpret_cast<uint4 (*)[kRows * kSegs]>(slab_mem);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
-  const int ks = blockIdx.y;
   const int kb = ks * kc, ke = min(g.d_in, kb + kc);
   const int r = tl.rank;
   const int n_batch = (ke - kb + kBatch - 1) / kBatch;
@@ -211,9 +223,27 @@ __device__ __forceinline__ void shrink_tile(const Geom& g, const SgTile& tl,
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       const int n = cb * 16 + li;
-      if (n < r) dst[n] = acc[cb][q];
+      if (n >= r) continue;
+      if constexpr (kCoherent)
+        __hip_atomic_store(dst + n, acc[cb][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        dst[n] = acc[cb][q];
     }
   }
+}
+
+// The narrowest shrink body that holds the tile's rank, within a launch whose widest is NBM.
+template <int DT, int NBM, bool kCoherent>
+__device__ __forceinline__ void shrink_any(const Geom& g, const SgTile& tl,
+                                           const int32_t* __restrict__ tok, int32_t kc,
+                                           const uint16_t* __restrict__ x, float* vpart,
+                                           int32_t v_stride, int64_t split_stride, int ks,
+                                           uint4* slab) {
+  const int nb = shrink_nb(tl.rank);
+  if (NBM >= 8 && nb == 8) shrink_tile<DT, NBM >= 8 ? 8 : NBM, kCoherent>(g, tl, tok, kc, x, vpart, v_stride, split_stride, ks, slab);
+  else if (NBM >= 4 && nb == 4) shrink_tile<DT, NBM >= 4 ? 4 : NBM, kCoherent>(g, tl, tok, kc, x, vpart, v_stride, split_stride, ks, slab);
+  else if (NBM >= 2 && nb == 2) shrink_tile<DT, NBM >= 2 ? 2 : NBM, kCoherent>(g, tl, tok, kc, x, vpart, v_stride, split_stride, ks, slab);
+  else shrink_tile<DT, 1, kCoherent>(g, tl, tok, kc, x, vpart, v_stride, split_stride, ks, slab);
 }
 
 // NBM: the widest template of the launch (its registers, LDS and occupancy); each tile
@@ -226,11 +256,7 @@ __global__ __launch_bounds__(64 * kWaves, shrink_waves(NBM)) void sgmv_shrink_ke
     int64_t split_stride) {
   __shared__ uint4 slab[2 * 16 * NBM * kSegs];
   const SgTile tl = tiles[blockIdx.x];
-  const int nb = shrink_nb(tl.rank);
-  if (NBM >= 8 && nb == 8) shrink_tile<DT, NBM >= 8 ? 8 : NBM>(g, tl, tok, kc, x, vpart, v_stride, split_stride, slab);
-  else if (NBM >= 4 && nb == 4) shrink_tile<DT, NBM >= 4 ? 4 : NBM>(g, tl, tok, kc, x, vpart, v_stride, split_stride, slab);
-  else if (NBM >= 2 && nb == 2) shrink_tile<DT, NBM >= 2 ? 2 : NBM>(g, tl, tok, kc, x, vpart, v_stride, split_stride, slab);
-  else shrink_tile<DT, 1>(g, tl, tok, kc, x, vpart, v_stride, split_stride, slab);
+  shrink_any<DT, NBM, false>(g, tl, tok, kc, x, vpart, v_stride, split_stride, (int)blockIdx.y, slab);
 }
 
 // ------------------------------------------------------------------ expand
@@ -246,12 +272,13 @@ constexpr int expand_bs_elems(int kb) { return expand_bbufs(kb) * kb * kChunkRow
 
 // One (tile, column block) with KB chunks of KS rows of the rank (rank <= KS * KB); KS is
 // the k of one product: 32 (16x16x32), or 16 (16x16x16) for ranks up to 16.
-template <int DT, int KB, int KS = kStep>
+// kCoherent: the partial sums are read at agent scope (written in the same launch).
+template <int DT, int KB, int KS = kStep, bool kCoherent = false>
 __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
                                             const int32_t* __restrict__ tok, int32_t ksplit,
                                             const float* __restrict__ vpart, int32_t v_stride,
                                             int64_t split_stride, uint16_t* __restrict__ y,
-                                            uint16_t* vs, uint16_t* bs) {
+                                            int cblock, uint16_t* vs, uint16_t* bs) {
   static_assert(KS == 16 || KS == 32, "k per product");
   constexpr int kRp = KB * KS;        // padded rank
   constexpr int kVPitch = kRp + 8;    // v row pitch in elements
@@ -260,7 +287,7 @@ __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kg = lane >> 4;
   const int r = tl.rank;
-  const int col_begin = blockIdx.y * (kSubPasses * kCols);
+  const int col_begin = cblock * (kSubPasses * kCols);
   const int n_pass = min(kSubPasses, (g.d_out - col_begin + kCols - 1) / kCols);
 
   int tk[4];  // token of operand row tb * 16 + li (the v^T operand's column)
@@ -333,7 +360,13 @@ __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
         a[sp] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (sp < ksplit && t >= 0 && kk < r) {
           const float* src = vpart + sp * split_stride + (int64_t)t * v_stride + kk;
-          if (vec) {
+          if constexpr (kCoherent) {  // 16-byte aligned rows (v_stride % 4 == 0 in apply calls)
+            const unsigned long long* q = reinterpret_cast<const unsigned long long*>(src);
+            const unsigned long long w0 = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned long long w1 = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a[sp] = make_float4(__uint_as_float((unsigned)w0), __uint_as_float((unsigned)(w0 >> 32)),
+                                __uint_as_float((unsigned)w1), __uint_as_float((unsigned)(w1 >> 32)));
+          } else if (vec) {
             a[sp] = *reinterpret_cast<const float4*>(src);
           } else {
             a[sp].x = src[0];
@@ -458,6 +491,23 @@ __device__ __forceinline__ void expand_tile(const Geom& g, const SgTile& tl,
   }
 }
 
+// The narrowest expand body that holds the tile's rank, within a launch whose widest is KBM
+// (the widest launch keeps its one body, see below).
+template <int DT, int KBM, bool kCoherent>
+__device__ __forceinline__ void expand_any(const Geom& g, const SgTile& tl,
+                                           const int32_t* __restrict__ tok, int32_t ksplit,
+                                           const float* vpart, int32_t v_stride,
+                                           int64_t split_stride, uint16_t* __restrict__ y,
+                                           int cblock, uint16_t* vs, uint16_t* bs) {
+  if constexpr (KBM >= 4) {
+    expand_tile<DT, 4, kStep, kCoherent>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, cblock, vs, bs);
+  } else {
+    if (KBM >= 2 && tl.rank > 32) expand_tile<DT, KBM, kStep, kCoherent>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, cblock, vs, bs);
+    else if (tl.rank > 16) expand_tile<DT, 1, kStep, kCoherent>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, cblock, vs, bs);
+    else expand_tile<DT, 1, 16, kCoherent>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, cblock, vs, bs);
+  }
+}
+
 // KBM: the widest template of the launch (its registers, LDS and occupancy); each tile
 // runs the narrowest one that holds its rank (uniform per workgroup, taken once). The
 // widest launch (ranks above 64) keeps its one body: next to the narrower bodies its
@@ -473,13 +523,63 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KBM)) void sgmv_expand_ke
   __shared__ uint16_t vs[expand_vs_elems(KBM)];
   __shared__ uint16_t bs[KBM >= 2 ? kBsMax : expand_bs_elems(1)];
   const SgTile tl = tiles[blockIdx.x];
-  if constexpr (KBM >= 4) {
-    expand_tile<DT, 4>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
-  } else {
-    if (KBM >= 2 && tl.rank > 32) expand_tile<DT, KBM>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
-    else if (tl.rank > 16) expand_tile<DT, 1>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
-    else expand_tile<DT, 1, 16>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, vs, bs);
+  expand_any<DT, KBM, false>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, (int)blockIdx.y, vs, bs);
+}
+
+// ------------------------------------------------------------------ fused (apply calls)
+// Shrink and expand of one projection in one launch. Workgroups [0, n_tiles * ksplit) are
+// shrink items (tile, k-range), tile-major; the rest are expand items (tile, column block),
+// tile-major. A shrink item stores its partial sums at agent scope, waits until they are
+// performed, then stores the call's tag into its flag word; an expand item polls its
+// tile's ksplit flags (bounded; a give-up is recorded in the workspace header) and reads
+// the partial sums at agent scope. Workgroups are dispatched in index order and shrink
+// items never wait, so every shrink item an expand item waits for has been dispatched
+// before it and finishes. The expand items take the slots the shrink items free at the
+// end of their phase, which two launches would leave idle.
+constexpr int fused_waves(int nbm, int kbm) {
+  return shrink_waves(nbm) < expand_waves(kbm) ? shrink_waves(nbm) : expand_waves(kbm);
+}
+template <int DT, int NBM, int KBM>
+__global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void sgmv_fused_kernel(
+    Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t kc,
+    int32_t ksplit, int32_t n_tiles, const uint16_t* __restrict__ x, float* vpart,
+    int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag, int32_t spin_limit,
+    unsigned long long* err, uint16_t* __restrict__ y) {
+  constexpr int kShrinkBytes = 2 * 16 * NBM * kSegs * 16;
+  constexpr int kBsMax = expand_bs_elems(KBM) > expand_bs_elems(2) ? expand_bs_elems(KBM) : expand_bs_elems(2);
+  constexpr int kVsElems = expand_vs_elems(KBM);
+  constexpr int kExpandBytes = (kVsElems + (KBM >= 2 ? kBsMax : expand_bs_elems(1))) * 2;
+  constexpr int kBytes = kShrinkBytes > kExpandBytes ? kShrinkBytes : kExpandBytes;
+  __shared__ uint4 lds[(kBytes + 15) / 16];
+  const int n_shrink = n_tiles * ksplit;
+  const int L = (int)blockIdx.x;
+  if (L < n_shrink) {
+    const SgTile tl = tiles[L / ksplit];
+    shrink_any<DT, NBM, true>(g, tl, tok, kc, x, vpart, v_stride, split_stride, L % ksplit, lds);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are performed
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flags + L, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
+  const int ncb = (g.d_out + kSubPasses * kCols - 1) / (kSubPasses * kCols);
+  const int E = L - n_shrink, t = E / ncb;
+  if (threadIdx.x < 64) {
+    const int lane = (int)threadIdx.x;
+    for (int spins = 0;; ++spins) {
+      const bool ok = lane >= ksplit ||
+                      __hip_atomic_load(flags + t * ksplit + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+      if (__all(ok)) break;
+      if (spins >= spin_limit) {
+        if (lane == 0) __hip_atomic_store(err, (unsigned long long)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  const SgTile tl = tiles[t];
+  uint16_t* vs = reinterpret_cast<uint16_t*>(lds);
+  expand_any<DT, KBM, true>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, E % ncb, vs, vs + kVsElems);
 }
 
 template <int DT>
@@ -513,7 +613,50 @@ hipError_t expand_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int
   return hipGetLastError();
 }
 
+template <int DT, int NBM, int KBM>
+hipError_t fused_launch(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
+                        int32_t ksplit, int32_t kc, const void* x, float* vpart, int32_t v_stride,
+                        int64_t split_stride, uint32_t* flags, uint32_t tag, int32_t spin_limit,
+                        unsigned long long* err, void* y, hipStream_t s, const LaunchEvents& ev) {
+  const int per_wg = kSubPasses * kCols;
+  const int64_t ncb = (g.d_out + per_wg - 1) / per_wg;
+  const int64_t n = (int64_t)n_tiles * ksplit + (int64_t)n_tiles * ncb;
+  if (n > INT32_MAX) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL((sgmv_fused_kernel<DT, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
+                        ev.start, ev.stop, 0, g, tiles, tok, kc, ksplit, n_tiles,
+                        (const uint16_t*)x, vpart, v_stride, split_stride, flags, tag, spin_limit,
+                        err, (uint16_t*)y);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t fused_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
+                    int32_t max_rank, int32_t ksplit, int32_t kc, const void* x, float* vpart,
+                    int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag,
+                    int32_t spin_limit, unsigned long long* err, void* y, hipStream_t s,
+                    const LaunchEvents& ev) {
+  if (max_rank <= 16) return fused_launch<DT, 1, 1>(g, tok, tiles, n_tiles, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  if (max_rank <= 32) return fused_launch<DT, 2, 1>(g, tok, tiles, n_tiles, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  if (max_rank <= 64) return fused_launch<DT, 4, 2>(g, tok, tiles, n_tiles, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  return fused_launch<DT, 8, 4>(g, tok, tiles, n_tiles, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+}
+
 }  // namespace
+
+hipError_t launch_sgmv_fused(const Geom& g, const int32_t* tok, const SgTile* tiles,
+                             int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
+                             const void* x, float* vpart, int32_t v_stride, int64_t split_stride,
+                             uint32_t* flags, uint32_t tag, int32_t spin_limit,
+                             unsigned long long* err, void* y, hipStream_t s,
+                             const LaunchEvents& ev) {
+  if (n_tiles <= 0) return hipSuccess;
+  if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit || kc % kRound ||
+      (v_stride & 3) || !flags || !err || tag == 0)
+    return hipErrorInvalidValue;
+  return g.dtype == SLORA_F16
+             ? fused_dt<SLORA_F16>(g, tok, tiles, n_tiles, max_rank, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev)
+             : fused_dt<SLORA_BF16>(g, tok, tiles, n_tiles, max_rank, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+}
 
 int sgmv_shrink_resident(int32_t max_rank, int32_t dtype) {
   static std::mutex mu;

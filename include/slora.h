@@ -343,17 +343,20 @@ int slora_expand(const slora_lora* lora, const slora_routing* routing, const flo
                  void* ws, int64_t ws_bytes, void* stream);
 
 /* Shrink + expand in one call (v lives in the workspace). y holds y0 on entry.
- * Decode tokens run in one launch: shrink workgroups publish v per group and the
- * group's expand workgroups wait for it (a bounded wait; see
- * slora_workspace_status). The work list is read by the kernels from a pinned
- * host staging ring owned by the library.
- * Two such decode launches resident on one device at once could each hold the
- * compute slots the other's shrink workgroups need, so the library orders them: a
- * call whose decode launch goes to another stream than the previous decode launch
- * on the device first makes its stream wait for the work queued on that previous
- * stream (an event recorded there; if that stream no longer exists, a device
- * synchronization). Decode launches from other processes sharing the device are
- * not ordered. */
+ * Each family runs in one launch: decode tokens' shrink workgroups publish v per
+ * group and the group's expand workgroups wait for it; prefill segments' shrink
+ * workgroups write their partial sums of a tile and a flag, and the tile's expand
+ * workgroups wait for every flag of the tile (bounded waits; see
+ * slora_workspace_status). Every shrink workgroup of a launch comes before its
+ * expand workgroups in dispatch order and never waits, so the waits end. The work
+ * list is read by the kernels from a pinned host staging ring owned by the library.
+ * Two such launches resident on one device at once could each hold the compute
+ * slots the other's shrink workgroups need, so the library orders them: a call
+ * whose launches go to another stream than the previous such call on the device
+ * first makes its stream wait for the work queued on that previous stream (an
+ * event recorded there; if that stream no longer exists, a device
+ * synchronization). Launches from other processes sharing the device are not
+ * ordered. */
 int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
                 void* ws, int64_t ws_bytes, void* stream);
 
@@ -364,9 +367,11 @@ int slora_apply(const slora_lora* lora, const slora_routing* routing, const void
  * padded with zero rows to the largest rank of the batch, and one padded batched GEMM
  * (the MFMA segment kernels over the copies, every adapter at the padded rank) produces
  * y. Results agree with slora_apply within rounding. The workspace (caller-owned, size
- * from slora_gathered_workspace_size, zero-filled once) holds the copies: n_requests x
- * r_pad x (ceil(d_in/P) + ceil(d_out/P)) pages. The routing's policy is ignored; no
- * launch of this path waits across workgroups, so it has no workspace status. */
+ * from slora_gathered_workspace_size, zero-filled once) holds the segment kernels' own
+ * workspace first, then the copies: n_requests x r_pad x (ceil(d_in/P) + ceil(d_out/P))
+ * pages. The routing's policy is ignored. The segment kernels run as in slora_apply (one
+ * launch whose expand workgroups wait for their tile's shrink workgroups), so a give-up
+ * is read with slora_workspace_status on this workspace. */
 int slora_gathered_workspace_size(const slora_lora* lora, const slora_routing* routing,
                                   int64_t* bytes);
 int slora_apply_gathered(const slora_lora* lora, const slora_routing* routing, const void* x,
@@ -376,8 +381,8 @@ int slora_apply_gathered(const slora_lora* lora, const slora_routing* routing, c
  * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments minus
  * the workspace, same kernels, same results bit for bit. The workspace is a static
  * device array of the library, 64 MiB on every GPU it runs on, held until the process
- * ends; a call that needs more (ws_layout: 256 + n_tokens * r_max * 8 bytes + the
- * prefill partial sums) is refused with SLORA_E_INVALID before anything runs, and so is
+ * ends; a call that needs more (256 + n_tokens * r_max * 8 bytes + the prefill
+ * partial sums + n_tokens * 32 bytes of prefill flags) is refused with SLORA_E_INVALID before anything runs, and so is
  * one whose work list would outgrow its 1 MiB staging slot. The call allocates no
  * device or pinned memory, except on its first call on a device, which also creates the
  * library's staging ring if no compute call has yet, resolves the array's address and
@@ -391,15 +396,16 @@ int slora_apply_noalloc(const slora_lora* lora, const slora_routing* routing, co
 
 /* Status of the slora_apply calls that used workspace ws since the previous status
  * read, once the work on `stream` has finished (this call synchronizes the stream):
- * 0 = clean; 1 = in at least one of them a decode workgroup gave up waiting for v
- * that another workgroup of the same launch should have published (that call's
- * results are not valid). The give-up is sticky in the workspace header until this
+ * 0 = clean; 1 = in at least one of them a workgroup gave up waiting for v (or a
+ * prefill tile's partial sums) that another workgroup of the same launch should have
+ * published (that call's results are not valid). The give-up is sticky in the workspace header until this
  * call reads it, and reading clears it. ws = NULL reads the current device's static
  * scratch of slora_apply_noalloc (0 if no such call has run on it). */
 int slora_workspace_status(void* ws, void* stream, int32_t* status);
 
-/* Bound of the wait in decode launches: an expand wave polls for its v at most `polls`
- * times before it gives up (see slora_workspace_status). polls = 0 restores the default
+/* Bound of the waits in slora_apply's launches: an expand wave polls for its v (decode
+ * tokens) or for its tile's flags (prefill segments) at most `polls` times before it
+ * gives up (see slora_workspace_status). polls = 0 restores the default
  * (2^20 polls, far beyond any wait a valid launch has). Applies to launches made after
  * the call, on every device. Tests of the give-up path set a small bound (1 poll: waves
  * that find v not yet published give up at once, so the launch ends with invalid
@@ -412,8 +418,9 @@ int slora_set_wait_limit(int32_t polls);
  * interval spans the kernel alone.
  * Recorded launches accumulate across enable / disable until slora_timing_read
  * returns and clears them, so a caller can time a sample of its calls. Kernel ids: SLORA_K_MBGMV_SHRINK,
- * SLORA_K_MBGMV_EXPAND, SLORA_K_SGMV_SHRINK, SLORA_K_SGMV_EXPAND, SLORA_K_MBGMV_FUSED (the decode
- * shrink and expand in one launch, as slora_apply runs them). */
+ * SLORA_K_MBGMV_EXPAND, SLORA_K_SGMV_SHRINK, SLORA_K_SGMV_EXPAND (the separate launches of
+ * slora_shrink and slora_expand), SLORA_K_MBGMV_FUSED and SLORA_K_SGMV_FUSED (shrink and expand
+ * in one launch, as slora_apply runs each family). */
 #define SLORA_K_MBGMV_SHRINK 0
 #define SLORA_K_MBGMV_EXPAND 1
 #define SLORA_K_SGMV_SHRINK 2
@@ -421,7 +428,8 @@ int slora_set_wait_limit(int32_t polls);
 #define SLORA_K_MBGMV_FUSED 4
 #define SLORA_K_GATHER 5 /* slora_apply_gathered's copy of the adapters out of the pool */
 #define SLORA_K_FETCH 6  /* slora_fetch_async / slora_fetch_many_async's copy into the pool */
-#define SLORA_K_COUNT 7
+#define SLORA_K_SGMV_FUSED 7
+#define SLORA_K_COUNT 8
 int slora_timing_enable(int32_t on);
 
 /* Waits for the recorded events, then writes per kernel id the number of timed

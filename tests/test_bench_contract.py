@@ -52,6 +52,6 @@ def test_bench_prints_one_json_line():
     assert d["device"]["compute_units"] > 0
     pf = d["prefill"]
     assert pf["workload"] == "prefill_sgmv" and pf["value"] > 0 and pf["workspace_status"] == "clean"
-    for kern in ("sgmv_shrink", "sgmv_expand"):
-        pr = pf["roofline"][kern]
-        assert pr["unit"] == "GB/s" and 0 < pr["frac"] < 1 and 0 < pr["mfma_frac"] < 1
+    pr = pf["roofline"]["sgmv_fused"]
+    assert pr["unit"] == "GB/s" and 0 < pr["frac"] < 1 and 0 < pr["mfma_frac"] < 1
+    assert set(pf["kernels"]) == {"sgmv_fused"}

@@ -33,6 +33,8 @@ def _gathered(rt, wl, proj=0, inst=None):
     ws = inst.gathered_workspace(call)
     inst.apply_gathered(call, x, y, ws)
     torch.cuda.synchronize()
+    from heterogeneous_lora_amd import _lib
+    assert _lib.workspace_status(ws.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
     return y.cpu().numpy().view(np.uint16), inst
 
 

@@ -566,15 +566,16 @@ def test_expand_probe_codes_bit_exact(rt, policy):
         inst.close()
 
 
-def test_wait_giveup_is_sticky_and_cleared(rt, decode7b):
-    """The decode launch's bounded wait, forced short from the host (every kernel still
-    ends normally): a give-up in any of several calls is reported by the next status
-    read, which clears it; with the default bound the same calls run clean and match
-    the oracle."""
+@pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
+def test_wait_giveup_is_sticky_and_cleared(rt, decode7b, policy):
+    """The fused launch's bounded wait (decode v for MBGMV, a tile's partial-sum flags for
+    SGMV), forced short from the host (every kernel still ends normally): a give-up in
+    any of several calls is reported by the next status read, which clears it; with the
+    default bound the same calls run clean and match the oracle."""
     from heterogeneous_lora_amd import _lib
     wl, inst = decode7b
-    say("[gpu] decode_7b with a 1-poll wait bound: give-ups reported, then cleared")
-    call = inst.call(0)
+    say(f"[gpu] decode_7b policy={POLICY_IDS[policy]} with a 1-poll wait bound: give-ups reported, then cleared")
+    call = inst.call(0, policy)
     x, y0 = inst.inputs(0)
     ws = inst.workspace(call)
     stream = torch.cuda.current_stream().cuda_stream
@@ -587,7 +588,7 @@ def test_wait_giveup_is_sticky_and_cleared(rt, decode7b):
         _lib.set_wait_limit(0)
     assert _lib.workspace_status(ws.data_ptr(), stream) == 1
     assert _lib.workspace_status(ws.data_ptr(), stream) == 0  # read once, then clear
-    say("[gpu] decode_7b with the default wait bound after the give-ups")
+    say(f"[gpu] decode_7b policy={POLICY_IDS[policy]} with the default wait bound after the give-ups")
     y = y0.clone()
     inst.apply(call, x, y, ws)
     assert _lib.workspace_status(ws.data_ptr(), stream) == 0
@@ -595,17 +596,18 @@ def test_wait_giveup_is_sticky_and_cleared(rt, decode7b):
     check_close(y.cpu().numpy().view(np.uint16), ref, wl.dtype, "decode_7b after give-ups")
 
 
-def test_two_stream_decode_applies(rt, decode7b):
-    """Decode applies of the 7B batch on two workspaces and two streams, issued
-    alternately with the host far ahead of the GPU: the library orders the fused
-    launches across the streams, every output matches the oracle and both workspaces
-    report a clean status."""
+@pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
+def test_two_stream_decode_applies(rt, decode7b, policy):
+    """Applies of the 7B decode batch on two workspaces and two streams, issued
+    alternately with the host far ahead of the GPU, through either family's fused
+    launch: the library orders the fused launches across the streams, every output
+    matches the oracle and both workspaces report a clean status."""
     wl, inst = decode7b
-    say("[gpu] decode_7b applies alternating over two streams")
+    say(f"[gpu] decode_7b policy={POLICY_IDS[policy]} applies alternating over two streams")
     ref, _ = oracle_ref(wl, 0)
     x, y0 = inst.inputs(0)
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    calls = [inst.call(0), inst.call(0)]
+    calls = [inst.call(0, policy), inst.call(0, policy)]
     wss = [inst.workspace(c) for c in calls]
     for s in streams:
         s.wait_stream(torch.cuda.current_stream())
