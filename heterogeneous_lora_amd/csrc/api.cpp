@@ -353,8 +353,11 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
       uint32_t* flags = (uint32_t*)(wsb + lay.flg_off);
       e = timed_launch(SLORA_K_SGMV_FUSED, s, [&](const LaunchEvents& le) {
         return by_rank(le, [&](int32_t t0, int32_t nt, int32_t mr, const LaunchEvents& l) {
+          // up to 2 * ksplit flags per tile (tiles of rank above 64 are shrunk in two
+          // row blocks), so each launch's flags start past every flag the tiles before
+          // it could use: a launch must never find the call's tag left by another
           return launch_sgmv_fused(g, pv.tok, pv.sg + t0, nt, mr, sp.ksplit, sp.kc, x, vpart,
-                                   v_stride, stride, flags + (int64_t)t0 * sp.ksplit, tag,
+                                   v_stride, stride, flags + 2 * (int64_t)t0 * sp.ksplit, tag,
                                    g_spin_limit, err, y, s, l);
         });
       });

@@ -124,7 +124,8 @@ void plan_write(const slora_lora* L, const slora_routing* R, PlanScratch* sc, vo
 //             slora_workspace_status reads and clears it)
 //   v_off: MBGMV v as uint64 words [n_tokens x r_max]: (tag << 32) | fp32 bits
 //   sg_off: SGMV partial v, fp32 [sg_max_split(d_in)][n_tokens x sg_v_stride(r_max)]
-//   flg_off: SGMV shrink flags, uint32 [n_tokens x kSgMaxSplit] (at most one tile per token)
+//   flg_off: SGMV shrink flags, uint32 [n_tokens x 2 x kSgMaxSplit] (at most one tile per
+//            token, at most two row blocks per tile)
 constexpr int64_t kHeaderBytes = 256;
 struct WsLayout {
   int64_t v_off, sg_off, flg_off, total;
@@ -186,8 +187,9 @@ hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* t
                               hipStream_t s, const LaunchEvents& ev = LaunchEvents());
 
 // Shrink and expand of an apply call in one launch: shrink items write their partial sums
-// and then their flag words (flags[tile * ksplit + range] = tag); expand items wait for
-// their tile's flags (spin_limit polls, a give-up recorded in *err). v_stride % 4 == 0.
+// and then their flag words (one per shrink item, at most 2 * ksplit per tile); expand
+// items wait for their tile's flags (spin_limit polls, a give-up recorded in *err).
+// v_stride % 4 == 0; tiles in descending rank (host-readable: the pinned work list).
 hipError_t launch_sgmv_fused(const Geom& g, const int32_t* tok, const SgTile* tiles,
                              int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
                              const void* x, float* vpart, int32_t v_stride, int64_t split_stride,

@@ -385,7 +385,7 @@ WsLayout ws_layout(const slora_lora* L, const slora_routing* R) {
   o.sg_off = o.v_off + align_up(rows * 8, 256);
   const int64_t sg_rows = T * sg_v_stride(std::max<int32_t>(L->r_max, 0));
   o.flg_off = o.sg_off + align_up((int64_t)sg_max_split(std::max<int32_t>(L->d_in, 0)) * sg_rows * 4, 256);
-  o.total = o.flg_off + align_up(T * kSgMaxSplit * 4, 256);
+  o.total = o.flg_off + align_up(T * 2 * kSgMaxSplit * 4, 256);
   return o;
 }
 

@@ -113,15 +113,16 @@ constexpr int32_t kSgMinSplit = 3;
 // 16-row blocks of rank rows the shrink template for ranks up to max_rank holds.
 constexpr int shrink_nb(int max_rank) { return max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8; }
 
-// One (tile, k-range) with NB 16-row blocks; slab holds 2 x 16 NB x kSegs vectors.
-// kCoherent: the partial sums are stored at agent scope (performed at the device's
-// coherence point), for a reader in the same launch.
+// One (tile, k-range) with NB 16-row blocks of rank rows from row0 on; slab holds
+// 2 x 16 NB x kSegs vectors. kCoherent: the partial sums are stored at agent scope
+// (performed at the device's coherence point), for a reader in the same launch.
 template <int DT, int NB, bool kCoherent = false>
 __device__ __forceinline__ void shrink_tile(const Geom& g, const SgTile& tl,
                                             const int32_t* __restrict__ tok, int32_t kc,
                                             const uint16_t* __restrict__ x,
                                             float* __restrict__ vpart, int32_t v_stride,
-                                            int64_t split_stride, int ks, uint4* slab_mem) {
+                                            int64_t split_stride, int ks, uint4* slab_mem,
+                                            int row0 = 0) {
   constexpr int kRows = 16 * NB;
   constexpr int kLoads = kRows * kSegs / (64 * kWaves);  // slab vectors per thread
   static_assert(kLoads >= 1 && kRows * kSegs == kLoads * 64 * kWaves, "slab split");
@@ -148,7 +149,7 @@ __device__ __forceinline__ void shrink_tile(const Geom& g, const SgTile& tl,
     if (live && c != cur_c) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const int n = i * 16 + srow;
+        const int n = row0 + i * 16 + srow;
         const uint16_t* p = fill_zero();
         bool real = false;
         if (n < r && c < g.cA) {
@@ -222,7 +223,7 @@ __device__ __forceinline__ void shrink_tile(const Geom& g, const SgTile& tl,
     float* dst = vpart + ks * split_stride + (int64_t)t * v_stride;
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-      const int n = cb * 16 + li;
+      const int n = row0 + cb * 16 + li;
       if (n >= r) continue;
       if constexpr (kCoherent)
         __hip_atomic_store(dst + n, acc[cb][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -527,35 +528,50 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KBM)) void sgmv_expand_ke
 }
 
 // ------------------------------------------------------------------ fused (apply calls)
-// Shrink and expand of one projection in one launch. Workgroups [0, n_tiles * ksplit) are
-// shrink items (tile, k-range), tile-major; the rest are expand items (tile, column block),
-// tile-major. A shrink item stores its partial sums at agent scope, waits until they are
-// performed, then stores the call's tag into its flag word; an expand item polls its
-// tile's ksplit flags (bounded; a give-up is recorded in the workspace header) and reads
-// the partial sums at agent scope. Workgroups are dispatched in index order and shrink
-// items never wait, so every shrink item an expand item waits for has been dispatched
-// before it and finishes. The expand items take the slots the shrink items free at the
-// end of their phase, which two launches would leave idle.
+// Shrink and expand of one projection in one launch. The first workgroups are shrink
+// items, the rest expand items (tile, column block), tile-major. Shrink items are
+// (tile, k-range) with one exception: in a launch over ranks above 64 (NBM = 4, KBM = 4),
+// each of the first n_wide tiles (those of rank above 64; tiles come in descending rank)
+// is shrunk as two 64-row blocks, items (tile, block, k-range), so that the launch needs
+// the 64-row shrink body only and keeps the expand's occupancy (3 workgroups per CU,
+// where the 128-row body's 64 KB slab allows 2). Each block writes its own rows of the
+// k-range's partial sums. Shrink item i stores its partial sums at agent scope, waits
+// until they are performed, then stores the call's tag into flags[i]; an expand item
+// polls its tile's flags (bounded; a give-up is recorded in the workspace header) and
+// reads the partial sums at agent scope. Workgroups are dispatched in index order and
+// shrink items never wait, so every shrink item an expand item waits for has been
+// dispatched before it and finishes. The expand items take the slots the shrink items
+// free at the end of their phase, which two launches would leave idle.
 constexpr int fused_waves(int nbm, int kbm) {
   return shrink_waves(nbm) < expand_waves(kbm) ? shrink_waves(nbm) : expand_waves(kbm);
 }
 template <int DT, int NBM, int KBM>
 __global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void sgmv_fused_kernel(
     Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t kc,
-    int32_t ksplit, int32_t n_tiles, const uint16_t* __restrict__ x, float* vpart,
-    int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag, int32_t spin_limit,
-    unsigned long long* err, uint16_t* __restrict__ y) {
+    int32_t ksplit, int32_t n_tiles, int32_t n_wide, const uint16_t* __restrict__ x,
+    float* vpart, int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag,
+    int32_t spin_limit, unsigned long long* err, uint16_t* __restrict__ y) {
+  constexpr bool kWide = NBM == 4 && KBM == 4;
   constexpr int kShrinkBytes = 2 * 16 * NBM * kSegs * 16;
   constexpr int kBsMax = expand_bs_elems(KBM) > expand_bs_elems(2) ? expand_bs_elems(KBM) : expand_bs_elems(2);
   constexpr int kVsElems = expand_vs_elems(KBM);
   constexpr int kExpandBytes = (kVsElems + (KBM >= 2 ? kBsMax : expand_bs_elems(1))) * 2;
   constexpr int kBytes = kShrinkBytes > kExpandBytes ? kShrinkBytes : kExpandBytes;
   __shared__ uint4 lds[(kBytes + 15) / 16];
-  const int n_shrink = n_tiles * ksplit;
+  const int nw = kWide ? n_wide : 0;
+  const int n_wide_items = 2 * nw * ksplit;
+  const int n_shrink = n_wide_items + (n_tiles - nw) * ksplit;
   const int L = (int)blockIdx.x;
   if (L < n_shrink) {
-    const SgTile tl = tiles[L / ksplit];
-    shrink_any<DT, NBM, true>(g, tl, tok, kc, x, vpart, v_stride, split_stride, L % ksplit, lds);
+    if (kWide && L < n_wide_items) {
+      const SgTile tl = tiles[L / (2 * ksplit)];
+      shrink_tile<DT, 4, true>(g, tl, tok, kc, x, vpart, v_stride, split_stride, L % ksplit, lds,
+                               64 * ((L / ksplit) & 1));
+    } else {
+      const int l2 = L - n_wide_items;
+      const SgTile tl = tiles[nw + l2 / ksplit];
+      shrink_any<DT, NBM, true>(g, tl, tok, kc, x, vpart, v_stride, split_stride, l2 % ksplit, lds);
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are performed
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_store(flags + L, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -563,11 +579,13 @@ __global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void sgmv_fused
   }
   const int ncb = (g.d_out + kSubPasses * kCols - 1) / (kSubPasses * kCols);
   const int E = L - n_shrink, t = E / ncb;
+  const int f0 = t < nw ? 2 * t * ksplit : n_wide_items + (t - nw) * ksplit;
+  const int nf = t < nw ? 2 * ksplit : ksplit;
   if (threadIdx.x < 64) {
     const int lane = (int)threadIdx.x;
     for (int spins = 0;; ++spins) {
-      const bool ok = lane >= ksplit ||
-                      __hip_atomic_load(flags + t * ksplit + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+      const bool ok = lane >= nf ||
+                      __hip_atomic_load(flags + f0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
       if (__all(ok)) break;
       if (spins >= spin_limit) {
         if (lane == 0) __hip_atomic_store(err, (unsigned long long)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -615,15 +633,16 @@ hipError_t expand_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int
 
 template <int DT, int NBM, int KBM>
 hipError_t fused_launch(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
-                        int32_t ksplit, int32_t kc, const void* x, float* vpart, int32_t v_stride,
-                        int64_t split_stride, uint32_t* flags, uint32_t tag, int32_t spin_limit,
-                        unsigned long long* err, void* y, hipStream_t s, const LaunchEvents& ev) {
+                        int32_t n_wide, int32_t ksplit, int32_t kc, const void* x, float* vpart,
+                        int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag,
+                        int32_t spin_limit, unsigned long long* err, void* y, hipStream_t s,
+                        const LaunchEvents& ev) {
   const int per_wg = kSubPasses * kCols;
   const int64_t ncb = (g.d_out + per_wg - 1) / per_wg;
-  const int64_t n = (int64_t)n_tiles * ksplit + (int64_t)n_tiles * ncb;
+  const int64_t n = (int64_t)(n_tiles + n_wide) * ksplit + (int64_t)n_tiles * ncb;
   if (n > INT32_MAX) return hipErrorInvalidValue;
   hipExtLaunchKernelGGL((sgmv_fused_kernel<DT, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
-                        ev.start, ev.stop, 0, g, tiles, tok, kc, ksplit, n_tiles,
+                        ev.start, ev.stop, 0, g, tiles, tok, kc, ksplit, n_tiles, n_wide,
                         (const uint16_t*)x, vpart, v_stride, split_stride, flags, tag, spin_limit,
                         err, (uint16_t*)y);
   return hipGetLastError();
@@ -635,10 +654,20 @@ hipError_t fused_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int3
                     int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag,
                     int32_t spin_limit, unsigned long long* err, void* y, hipStream_t s,
                     const LaunchEvents& ev) {
-  if (max_rank <= 16) return fused_launch<DT, 1, 1>(g, tok, tiles, n_tiles, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
-  if (max_rank <= 32) return fused_launch<DT, 2, 1>(g, tok, tiles, n_tiles, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
-  if (max_rank <= 64) return fused_launch<DT, 4, 2>(g, tok, tiles, n_tiles, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
-  return fused_launch<DT, 8, 4>(g, tok, tiles, n_tiles, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  if (max_rank <= 16) return fused_launch<DT, 1, 1>(g, tok, tiles, n_tiles, 0, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  if (max_rank <= 32) return fused_launch<DT, 2, 1>(g, tok, tiles, n_tiles, 0, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  if (max_rank <= 64) return fused_launch<DT, 4, 2>(g, tok, tiles, n_tiles, 0, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  // ranks above 64: the tiles that have them come first (descending rank; the tile
+  // records are in host-visible pinned memory). Beside narrower tiles they are shrunk in
+  // two 64-row blocks, so that the whole launch keeps 3 workgroups per CU; a launch of
+  // such tiles alone keeps the 128-row body, which reads each x row once.
+  int32_t n_wide = 0;
+  while (n_wide < n_tiles && tiles[n_wide].rank > 64) ++n_wide;
+  for (int32_t i = n_wide; i < n_tiles; ++i)
+    if (tiles[i].rank > 64) return hipErrorInvalidValue;
+  if (n_wide == n_tiles)
+    return fused_launch<DT, 8, 4>(g, tok, tiles, n_tiles, 0, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  return fused_launch<DT, 4, 4>(g, tok, tiles, n_tiles, n_wide, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
 }
 
 }  // namespace

@@ -382,8 +382,9 @@ int slora_apply_gathered(const slora_lora* lora, const slora_routing* routing, c
  * the workspace, same kernels, same results bit for bit. The workspace is a static
  * device array of the library, 64 MiB on every GPU it runs on, held until the process
  * ends; a call that needs more (256 + n_tokens * r_max * 8 bytes + the prefill
- * partial sums + n_tokens * 32 bytes of prefill flags) is refused with SLORA_E_INVALID before anything runs, and so is
- * one whose work list would outgrow its 1 MiB staging slot. The call allocates no
+ * partial sums + n_tokens * 64 bytes of prefill flags, each part rounded up to 256
+ * bytes) is refused with SLORA_E_INVALID before anything runs, and so is one whose
+ * work list would outgrow its 1 MiB staging slot. The call allocates no
  * device or pinned memory, except on its first call on a device, which also creates the
  * library's staging ring if no compute call has yet, resolves the array's address and
  * clears the array on `stream`. Every call on a GPU shares that GPU's array, which keeps
