@@ -69,14 +69,17 @@ def algorithmic(wl, proj, call):
                                   flops=int(2 * tok_r * p.d_out), tokens=T, adapters=len(rank_of))
         out[f + "_fused"] = {k: out[f + "_shrink"][k] + out[f + "_expand"][k] for k in ("bytes", "flops")}
         out[f + "_fused"].update(tokens=T, adapters=len(rank_of))
+    # both families in one launch (a call with decode groups and segments in one launch)
+    out["mixed_fused"] = {k: out["mbgmv_fused"][k] + out["sgmv_fused"][k]
+                          for k in ("bytes", "flops", "tokens", "adapters")}
     return out
 
 
 # Source files each kernel family is compiled from (a counter summary is void once they change).
 KERNEL_SOURCES = {
-    fam: [f"heterogeneous_lora_amd/csrc/{fam}.hip", "heterogeneous_lora_amd/csrc/device_common.h",
-          "heterogeneous_lora_amd/csrc/internal.h"]
-    for fam in ("mbgmv", "sgmv")
+    fam: [f"heterogeneous_lora_amd/csrc/{src}.hip", "heterogeneous_lora_amd/csrc/mbgmv_dev.h",
+          "heterogeneous_lora_amd/csrc/device_common.h", "heterogeneous_lora_amd/csrc/internal.h"]
+    for fam, src in (("mbgmv", "mbgmv"), ("sgmv", "sgmv"), ("mixed", "sgmv"))
 }
 
 

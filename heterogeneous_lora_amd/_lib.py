@@ -450,7 +450,7 @@ def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int,
 
 
 KERNELS = ["mbgmv_shrink", "mbgmv_expand", "sgmv_shrink", "sgmv_expand", "mbgmv_fused", "gather",
-           "fetch", "sgmv_fused"]
+           "fetch", "sgmv_fused", "mixed_fused"]
 
 
 def timing_enable(on: bool):

@@ -305,6 +305,7 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
   const float* vr = mode == kApply ? v : v_in;
   hipError_t e = hipSuccess;
   uint32_t tag = 0;
+  bool mb_done = false;  // the decode groups ran in the segments' launch
   if (mode == kApply && (pv.n_mb || pv.n_sg)) {
     // A fresh tag per fused call on this workspace; before a tag could repeat, the
     // workspace past its header is cleared so no stale word can carry it (the header
@@ -351,7 +352,13 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
     };
     if (mode == kApply) {
       uint32_t* flags = (uint32_t*)(wsb + lay.flg_off);
-      e = timed_launch(SLORA_K_SGMV_FUSED, s, [&](const LaunchEvents& le) {
+      // decode groups too, and the segments in one launch: both families in that launch
+      mb_done = pv.n_mb > 0 && !split;
+      e = timed_launch(mb_done ? SLORA_K_MIXED_FUSED : SLORA_K_SGMV_FUSED, s, [&](const LaunchEvents& le) {
+        if (mb_done)
+          return launch_sgmv_fused(g, pv.tok, pv.sg, pv.n_sg, pv.sg_max_rank, sp.ksplit, sp.kc, x,
+                                   vpart, v_stride, stride, flags, tag, g_spin_limit, err, y, s, le,
+                                   pv.mb, pv.n_mb, pv.n_mb_shrink, pv.mb_max_tok, v);
         return by_rank(le, [&](int32_t t0, int32_t nt, int32_t mr, const LaunchEvents& l) {
           // up to 2 * ksplit flags per tile (tiles of rank above 64 are shrunk in two
           // row blocks), so each launch's flags start past every flag the tiles before
@@ -381,7 +388,7 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
       if (e != hipSuccess) return hip_fail(e, "sgmv_expand launch");
     }
   }
-  if (pv.n_mb) {
+  if (pv.n_mb && !mb_done) {
     const bool has_expand = pv.n_mb > pv.n_mb_shrink;
     if (mode == kApply) {
       e = timed_launch(SLORA_K_MBGMV_FUSED, s, [&](const LaunchEvents& le) {

@@ -190,12 +190,17 @@ hipError_t launch_sgmv_expand(const Geom& g, const int32_t* tok, const SgTile* t
 // and then their flag words (one per shrink item, at most 2 * ksplit per tile); expand
 // items wait for their tile's flags (spin_limit polls, a give-up recorded in *err).
 // v_stride % 4 == 0; tiles in descending rank (host-readable: the pinned work list).
+// With n_mb > 0 the call's MBGMV items (shrink items first, as launch_mbgmv takes them,
+// v_mb their tagged v) run in the same launch: every shrink item of both families
+// before every expand item.
 hipError_t launch_sgmv_fused(const Geom& g, const int32_t* tok, const SgTile* tiles,
                              int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
                              const void* x, float* vpart, int32_t v_stride, int64_t split_stride,
                              uint32_t* flags, uint32_t tag, int32_t spin_limit,
                              unsigned long long* err, void* y, hipStream_t s,
-                             const LaunchEvents& ev = LaunchEvents());
+                             const LaunchEvents& ev = LaunchEvents(),
+                             const MbItem* mb_items = nullptr, int32_t n_mb = 0,
+                             int32_t n_mb_shrink = 0, int32_t mb_max_tok = 0, void* v_mb = nullptr);
 
 // Ablation baseline: copy each request's adapter out of the pool into contiguous,
 // rank-padded memory (gather.hip). One entry per request.

@@ -42,6 +42,7 @@
 #include <tuple>
 
 #include "device_common.h"
+#include "mbgmv_dev.h"
 
 namespace slora {
 namespace {
@@ -545,47 +546,73 @@ __global__ __launch_bounds__(64 * kWaves, expand_waves(KBM)) void sgmv_expand_ke
 constexpr int fused_waves(int nbm, int kbm) {
   return shrink_waves(nbm) < expand_waves(kbm) ? shrink_waves(nbm) : expand_waves(kbm);
 }
+// LDS of a fused launch: the larger of its shrink slab and its expand stages (v rows,
+// then B stages sized as the expand kernel sizes them).
+constexpr int fused_lds_bytes(int nbm, int kbm) {
+  const int slab = 2 * 16 * nbm * kSegs * 16;
+  const int bs_wide = expand_bs_elems(kbm) > expand_bs_elems(2) ? expand_bs_elems(kbm) : expand_bs_elems(2);
+  const int stages = (expand_vs_elems(kbm) + (kbm >= 2 ? bs_wide : expand_bs_elems(1))) * 2;
+  return slab > stages ? slab : stages;
+}
+
+// A fused launch's segment work (kernel arguments). n_wide: the leading tiles shrunk in
+// two 64-row blocks (used only by the NBM = 4, KBM = 4 template).
+struct SgWork {
+  const SgTile* tiles;
+  const int32_t* tok;
+  int32_t kc, ksplit, n_tiles, n_wide;
+  float* vpart;
+  int32_t v_stride;
+  int64_t split_stride;
+  uint32_t* flags;
+};
+
+template <int NBM, int KBM>
+__device__ __forceinline__ int sg_wide(const SgWork& w) { return NBM == 4 && KBM == 4 ? w.n_wide : 0; }
+template <int NBM, int KBM>
+__device__ __forceinline__ int sg_shrink_items(const SgWork& w) { return (w.n_tiles + sg_wide<NBM, KBM>(w)) * w.ksplit; }
+__device__ __forceinline__ int sg_expand_blocks(const Geom& g) {
+  return (g.d_out + kSubPasses * kCols - 1) / (kSubPasses * kCols);
+}
+
+// Shrink item L: its partial sums, then its flag word.
 template <int DT, int NBM, int KBM>
-__global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void sgmv_fused_kernel(
-    Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t kc,
-    int32_t ksplit, int32_t n_tiles, int32_t n_wide, const uint16_t* __restrict__ x,
-    float* vpart, int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag,
-    int32_t spin_limit, unsigned long long* err, uint16_t* __restrict__ y) {
-  constexpr bool kWide = NBM == 4 && KBM == 4;
-  constexpr int kShrinkBytes = 2 * 16 * NBM * kSegs * 16;
-  constexpr int kBsMax = expand_bs_elems(KBM) > expand_bs_elems(2) ? expand_bs_elems(KBM) : expand_bs_elems(2);
-  constexpr int kVsElems = expand_vs_elems(KBM);
-  constexpr int kExpandBytes = (kVsElems + (KBM >= 2 ? kBsMax : expand_bs_elems(1))) * 2;
-  constexpr int kBytes = kShrinkBytes > kExpandBytes ? kShrinkBytes : kExpandBytes;
-  __shared__ uint4 lds[(kBytes + 15) / 16];
-  const int nw = kWide ? n_wide : 0;
-  const int n_wide_items = 2 * nw * ksplit;
-  const int n_shrink = n_wide_items + (n_tiles - nw) * ksplit;
-  const int L = (int)blockIdx.x;
-  if (L < n_shrink) {
-    if (kWide && L < n_wide_items) {
-      const SgTile tl = tiles[L / (2 * ksplit)];
-      shrink_tile<DT, 4, true>(g, tl, tok, kc, x, vpart, v_stride, split_stride, L % ksplit, lds,
-                               64 * ((L / ksplit) & 1));
-    } else {
-      const int l2 = L - n_wide_items;
-      const SgTile tl = tiles[nw + l2 / ksplit];
-      shrink_any<DT, NBM, true>(g, tl, tok, kc, x, vpart, v_stride, split_stride, l2 % ksplit, lds);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are performed
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flags + L, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
+__device__ __forceinline__ void sg_shrink_item(const Geom& g, const SgWork& w,
+                                               const uint16_t* __restrict__ x, uint32_t tag, int L,
+                                               uint4* lds) {
+  const int nw = sg_wide<NBM, KBM>(w);
+  const int n_wide_items = 2 * nw * w.ksplit;
+  if (NBM == 4 && KBM == 4 && L < n_wide_items) {
+    const SgTile tl = w.tiles[L / (2 * w.ksplit)];
+    shrink_tile<DT, 4, true>(g, tl, w.tok, w.kc, x, w.vpart, w.v_stride, w.split_stride,
+                             L % w.ksplit, lds, 64 * ((L / w.ksplit) & 1));
+  } else {
+    const int l2 = L - n_wide_items;
+    const SgTile tl = w.tiles[nw + l2 / w.ksplit];
+    shrink_any<DT, NBM, true>(g, tl, w.tok, w.kc, x, w.vpart, w.v_stride, w.split_stride,
+                              l2 % w.ksplit, lds);
   }
-  const int ncb = (g.d_out + kSubPasses * kCols - 1) / (kSubPasses * kCols);
-  const int E = L - n_shrink, t = E / ncb;
-  const int f0 = t < nw ? 2 * t * ksplit : n_wide_items + (t - nw) * ksplit;
-  const int nf = t < nw ? 2 * ksplit : ksplit;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are performed
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(w.flags + L, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Expand item E (tile E / column blocks, column block E % column blocks): waits for the
+// tile's flags, then expands.
+template <int DT, int NBM, int KBM>
+__device__ __forceinline__ void sg_expand_item(const Geom& g, const SgWork& w, uint32_t tag,
+                                               int32_t spin_limit, unsigned long long* err,
+                                               uint16_t* __restrict__ y, int E, uint4* lds) {
+  const int nw = sg_wide<NBM, KBM>(w);
+  const int ncb = sg_expand_blocks(g);
+  const int t = E / ncb;
+  const int f0 = t < nw ? 2 * t * w.ksplit : 2 * nw * w.ksplit + (t - nw) * w.ksplit;
+  const int nf = t < nw ? 2 * w.ksplit : w.ksplit;
   if (threadIdx.x < 64) {
     const int lane = (int)threadIdx.x;
     for (int spins = 0;; ++spins) {
       const bool ok = lane >= nf ||
-                      __hip_atomic_load(flags + f0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+                      __hip_atomic_load(w.flags + f0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
       if (__all(ok)) break;
       if (spins >= spin_limit) {
         if (lane == 0) __hip_atomic_store(err, (unsigned long long)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -595,9 +622,61 @@ __global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void sgmv_fused
     }
   }
   __syncthreads();
-  const SgTile tl = tiles[t];
+  const SgTile tl = w.tiles[t];
   uint16_t* vs = reinterpret_cast<uint16_t*>(lds);
-  expand_any<DT, KBM, true>(g, tl, tok, ksplit, vpart, v_stride, split_stride, y, E % ncb, vs, vs + kVsElems);
+  expand_any<DT, KBM, true>(g, tl, w.tok, w.ksplit, w.vpart, w.v_stride, w.split_stride, y, E % ncb,
+                            vs, vs + expand_vs_elems(KBM));
+}
+
+template <int DT, int NBM, int KBM>
+__global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void sgmv_fused_kernel(
+    Geom g, const SgTile* __restrict__ tiles, const int32_t* __restrict__ tok, int32_t kc,
+    int32_t ksplit, int32_t n_tiles, int32_t n_wide, const uint16_t* __restrict__ x,
+    float* vpart, int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag,
+    int32_t spin_limit, unsigned long long* err, uint16_t* __restrict__ y) {
+  __shared__ uint4 lds[(fused_lds_bytes(NBM, KBM) + 15) / 16];
+  const SgWork w{tiles, tok, kc, ksplit, n_tiles, n_wide, vpart, v_stride, split_stride, flags};
+  const int L = (int)blockIdx.x;
+  const int n_shrink = sg_shrink_items<NBM, KBM>(w);
+  if (L < n_shrink) sg_shrink_item<DT, NBM, KBM>(g, w, x, tag, L, lds);
+  else sg_expand_item<DT, NBM, KBM>(g, w, tag, spin_limit, err, y, L - n_shrink, lds);
+}
+
+// ------------------------------------------------------------------ both families (apply calls)
+// A call with decode groups (MBGMV items) and segment tiles runs both families in one
+// launch, so that one family's ramp and tail overlap the other's work and the stream
+// has one launch instead of two: workgroups [MBGMV shrink items][segment shrink items]
+// [MBGMV expand items][segment expand items]. Every shrink item of either family comes
+// before every expand item and none waits, so the in-order-dispatch argument holds for
+// both hand-offs (v words for MBGMV, flags for the segments); they share the call's tag
+// and the workspace header's give-up word. LDS is the larger of the two families' needs.
+template <int DT, bool kUniformChunk, int NBM, int KBM>
+__global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void mixed_fused_kernel(
+    Geom g, SgWork w, const MbItem* __restrict__ items, int32_t n_mb, int32_t n_mb_shrink,
+    const uint16_t* __restrict__ x, void* v_mb, uint32_t tag, int32_t spin_limit,
+    unsigned long long* err, uint16_t* __restrict__ y) {
+  constexpr int kMbBytes = mb::kRedBytes > kMbGroup * mb::kBatchVecs * 16 ? mb::kRedBytes : kMbGroup * mb::kBatchVecs * 16;
+  constexpr int kBytes = fused_lds_bytes(NBM, KBM) > kMbBytes ? fused_lds_bytes(NBM, KBM) : kMbBytes;
+  __shared__ uint4 lds[(kBytes + 15) / 16];
+  int L = (int)blockIdx.x;
+  if (L < n_mb_shrink) {
+    const MbItem it = items[L];
+    mb::run_item<DT, kUniformChunk, true>(g, it, x, v_mb, y, tag, err, spin_limit, lds);
+    return;
+  }
+  L -= n_mb_shrink;
+  const int sg_shrink = sg_shrink_items<NBM, KBM>(w);
+  if (L < sg_shrink) {
+    sg_shrink_item<DT, NBM, KBM>(g, w, x, tag, L, lds);
+    return;
+  }
+  L -= sg_shrink;
+  if (L < n_mb - n_mb_shrink) {
+    const MbItem it = items[n_mb_shrink + L];
+    mb::run_item<DT, kUniformChunk, true>(g, it, x, v_mb, y, tag, err, spin_limit, lds);
+    return;
+  }
+  sg_expand_item<DT, NBM, KBM>(g, w, tag, spin_limit, err, y, L - (n_mb - n_mb_shrink), lds);
 }
 
 template <int DT>
@@ -631,43 +710,62 @@ hipError_t expand_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int
   return hipGetLastError();
 }
 
+// Both launchers: the grid, the segment work and, for a launch of both families, the
+// MBGMV items (n_mb = 0: segments only).
+struct MbPart {
+  const MbItem* items;
+  int32_t n_mb, n_mb_shrink;
+  void* v;
+};
+
 template <int DT, int NBM, int KBM>
-hipError_t fused_launch(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
-                        int32_t n_wide, int32_t ksplit, int32_t kc, const void* x, float* vpart,
-                        int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag,
-                        int32_t spin_limit, unsigned long long* err, void* y, hipStream_t s,
-                        const LaunchEvents& ev) {
+hipError_t fused_launch(const Geom& g, const SgWork& w, const MbPart& mp, const void* x,
+                        uint32_t tag, int32_t spin_limit, unsigned long long* err, void* y,
+                        hipStream_t s, const LaunchEvents& ev) {
   const int per_wg = kSubPasses * kCols;
   const int64_t ncb = (g.d_out + per_wg - 1) / per_wg;
-  const int64_t n = (int64_t)(n_tiles + n_wide) * ksplit + (int64_t)n_tiles * ncb;
+  const int64_t wide = NBM == 4 && KBM == 4 ? w.n_wide : 0;
+  const int64_t n = (int64_t)(w.n_tiles + wide) * w.ksplit + (int64_t)w.n_tiles * ncb + mp.n_mb;
   if (n > INT32_MAX) return hipErrorInvalidValue;
-  hipExtLaunchKernelGGL((sgmv_fused_kernel<DT, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
-                        ev.start, ev.stop, 0, g, tiles, tok, kc, ksplit, n_tiles, n_wide,
-                        (const uint16_t*)x, vpart, v_stride, split_stride, flags, tag, spin_limit,
-                        err, (uint16_t*)y);
+  const uint16_t* xp = (const uint16_t*)x;
+  uint16_t* yp = (uint16_t*)y;
+  if (mp.n_mb == 0) {
+    hipExtLaunchKernelGGL((sgmv_fused_kernel<DT, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
+                          ev.start, ev.stop, 0, g, w.tiles, w.tok, w.kc, w.ksplit, w.n_tiles, w.n_wide,
+                          xp, w.vpart, w.v_stride, w.split_stride, w.flags, tag, spin_limit, err, yp);
+    return hipGetLastError();
+  }
+  if constexpr (NBM == 8) {
+    return hipErrorInvalidValue;  // both families take the 3-per-CU wide template
+  } else if (g.P % 512 == 0)
+    hipExtLaunchKernelGGL((mixed_fused_kernel<DT, true, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
+                          ev.start, ev.stop, 0, g, w, mp.items, mp.n_mb, mp.n_mb_shrink, xp, mp.v, tag,
+                          spin_limit, err, yp);
+  else
+    hipExtLaunchKernelGGL((mixed_fused_kernel<DT, false, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
+                          ev.start, ev.stop, 0, g, w, mp.items, mp.n_mb, mp.n_mb_shrink, xp, mp.v, tag,
+                          spin_limit, err, yp);
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t fused_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int32_t n_tiles,
-                    int32_t max_rank, int32_t ksplit, int32_t kc, const void* x, float* vpart,
-                    int32_t v_stride, int64_t split_stride, uint32_t* flags, uint32_t tag,
-                    int32_t spin_limit, unsigned long long* err, void* y, hipStream_t s,
-                    const LaunchEvents& ev) {
-  if (max_rank <= 16) return fused_launch<DT, 1, 1>(g, tok, tiles, n_tiles, 0, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
-  if (max_rank <= 32) return fused_launch<DT, 2, 1>(g, tok, tiles, n_tiles, 0, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
-  if (max_rank <= 64) return fused_launch<DT, 4, 2>(g, tok, tiles, n_tiles, 0, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+hipError_t fused_dt(const Geom& g, SgWork w, int32_t max_rank, const MbPart& mp, const void* x,
+                    uint32_t tag, int32_t spin_limit, unsigned long long* err, void* y,
+                    hipStream_t s, const LaunchEvents& ev) {
+  w.n_wide = 0;
+  if (max_rank <= 16) return fused_launch<DT, 1, 1>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
+  if (max_rank <= 32) return fused_launch<DT, 2, 1>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
+  if (max_rank <= 64) return fused_launch<DT, 4, 2>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
   // ranks above 64: the tiles that have them come first (descending rank; the tile
   // records are in host-visible pinned memory). Beside narrower tiles they are shrunk in
   // two 64-row blocks, so that the whole launch keeps 3 workgroups per CU; a launch of
   // such tiles alone keeps the 128-row body, which reads each x row once.
-  int32_t n_wide = 0;
-  while (n_wide < n_tiles && tiles[n_wide].rank > 64) ++n_wide;
-  for (int32_t i = n_wide; i < n_tiles; ++i)
-    if (tiles[i].rank > 64) return hipErrorInvalidValue;
-  if (n_wide == n_tiles)
-    return fused_launch<DT, 8, 4>(g, tok, tiles, n_tiles, 0, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
-  return fused_launch<DT, 4, 4>(g, tok, tiles, n_tiles, n_wide, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+  while (w.n_wide < w.n_tiles && w.tiles[w.n_wide].rank > 64) ++w.n_wide;
+  for (int32_t i = w.n_wide; i < w.n_tiles; ++i)
+    if (w.tiles[i].rank > 64) return hipErrorInvalidValue;
+  if (w.n_wide == w.n_tiles && mp.n_mb == 0)
+    return fused_launch<DT, 8, 4>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
+  return fused_launch<DT, 4, 4>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
 }
 
 }  // namespace
@@ -677,14 +775,20 @@ hipError_t launch_sgmv_fused(const Geom& g, const int32_t* tok, const SgTile* ti
                              const void* x, float* vpart, int32_t v_stride, int64_t split_stride,
                              uint32_t* flags, uint32_t tag, int32_t spin_limit,
                              unsigned long long* err, void* y, hipStream_t s,
-                             const LaunchEvents& ev) {
+                             const LaunchEvents& ev, const MbItem* mb_items, int32_t n_mb,
+                             int32_t n_mb_shrink, int32_t mb_max_tok, void* v_mb) {
   if (n_tiles <= 0) return hipSuccess;
   if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit || kc % kRound ||
       (v_stride & 3) || !flags || !err || tag == 0)
     return hipErrorInvalidValue;
+  if (n_mb < 0 || n_mb_shrink < 0 || n_mb_shrink > n_mb ||
+      (n_mb > 0 && (!mb_items || !v_mb || mb_max_tok < 1 || mb_max_tok > kMbGroup)))
+    return hipErrorInvalidValue;
+  const SgWork w{tiles, tok, kc, ksplit, n_tiles, 0, vpart, v_stride, split_stride, flags};
+  const MbPart mp{mb_items, n_mb, n_mb_shrink, v_mb};
   return g.dtype == SLORA_F16
-             ? fused_dt<SLORA_F16>(g, tok, tiles, n_tiles, max_rank, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev)
-             : fused_dt<SLORA_BF16>(g, tok, tiles, n_tiles, max_rank, ksplit, kc, x, vpart, v_stride, split_stride, flags, tag, spin_limit, err, y, s, ev);
+             ? fused_dt<SLORA_F16>(g, w, max_rank, mp, x, tag, spin_limit, err, y, s, ev)
+             : fused_dt<SLORA_BF16>(g, w, max_rank, mp, x, tag, spin_limit, err, y, s, ev);
 }
 
 int sgmv_shrink_resident(int32_t max_rank, int32_t dtype) {

@@ -343,12 +343,13 @@ int slora_expand(const slora_lora* lora, const slora_routing* routing, const flo
                  void* ws, int64_t ws_bytes, void* stream);
 
 /* Shrink + expand in one call (v lives in the workspace). y holds y0 on entry.
- * Each family runs in one launch: decode tokens' shrink workgroups publish v per
- * group and the group's expand workgroups wait for it; prefill segments' shrink
- * workgroups write their partial sums of a tile and a flag, and the tile's expand
- * workgroups wait for every flag of the tile (bounded waits; see
- * slora_workspace_status). Every shrink workgroup of a launch comes before its
- * expand workgroups in dispatch order and never waits, so the waits end. The work
+ * Each family runs in one launch, and a call with both usually runs both in one:
+ * decode tokens' shrink workgroups publish v per group and the group's expand
+ * workgroups wait for it; prefill segments' shrink workgroups write their partial sums
+ * of a tile and a flag, and the tile's expand workgroups wait for every flag of the
+ * tile (bounded waits; see slora_workspace_status). Every shrink workgroup of a launch
+ * comes before its expand workgroups in dispatch order and never waits, so the waits
+ * end. The work
  * list is read by the kernels from a pinned host staging ring owned by the library.
  * Two such launches resident on one device at once could each hold the compute
  * slots the other's shrink workgroups need, so the library orders them: a call
@@ -421,7 +422,8 @@ int slora_set_wait_limit(int32_t polls);
  * returns and clears them, so a caller can time a sample of its calls. Kernel ids: SLORA_K_MBGMV_SHRINK,
  * SLORA_K_MBGMV_EXPAND, SLORA_K_SGMV_SHRINK, SLORA_K_SGMV_EXPAND (the separate launches of
  * slora_shrink and slora_expand), SLORA_K_MBGMV_FUSED and SLORA_K_SGMV_FUSED (shrink and expand
- * in one launch, as slora_apply runs each family). */
+ * in one launch, as slora_apply runs each family), SLORA_K_MIXED_FUSED (a call with both
+ * families whose segments fit one launch: everything in that launch). */
 #define SLORA_K_MBGMV_SHRINK 0
 #define SLORA_K_MBGMV_EXPAND 1
 #define SLORA_K_SGMV_SHRINK 2
@@ -430,7 +432,8 @@ int slora_set_wait_limit(int32_t polls);
 #define SLORA_K_GATHER 5 /* slora_apply_gathered's copy of the adapters out of the pool */
 #define SLORA_K_FETCH 6  /* slora_fetch_async / slora_fetch_many_async's copy into the pool */
 #define SLORA_K_SGMV_FUSED 7
-#define SLORA_K_COUNT 8
+#define SLORA_K_MIXED_FUSED 8 /* both families of one slora_apply in one launch */
+#define SLORA_K_COUNT 9
 int slora_timing_enable(int32_t on);
 
 /* Waits for the recorded events, then writes per kernel id the number of timed

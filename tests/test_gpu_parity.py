@@ -566,6 +566,48 @@ def test_expand_probe_codes_bit_exact(rt, policy):
         inst.close()
 
 
+# decode ids spread over many adapters (MBGMV groups) beside a few segments (SGMV tiles,
+# ranks to 128, too few for a launch per rank class)
+MIXED_ONE = dict(seed=122, dtype="f16", n_adapters=300, d_in=4096, d_out=4096, page_elems=4096,
+                 n_tokens=1024, n_segments=6, rank_choices=(8, 16, 64, 128), p_none=0.05)
+
+
+def test_mixed_call_one_launch(rt):
+    """A call with decode ids and segments under AUTO routing runs both families in one
+    launch (the timed kernels are one mixed_fused launch), matches the oracle on every row
+    with a clean status, and gives the same bits on a second call. (The give-up path of
+    each hand-off is forced in test_wait_giveup_is_sticky_and_cleared; in this launch the
+    segment expand items come last and find their flags already set.)"""
+    from heterogeneous_lora_amd import _lib
+    wl = workloads.random_small(**MIXED_ONE)
+    say(f"[gpu] mixed call in one launch: {wl.n_tokens} tokens, "
+        f"{int(wl.seg_offsets[-1])} in {len(wl.seg_adapter)} segments")
+    inst = rt.PagedLoRA(wl)
+    call = inst.call(0)
+    groups, _ = _lib.plan_inspect(call)
+    assert (groups[:, 0] == 0).any() and (groups[:, 0] == 1).any(), "both families expected"
+    assert (groups[groups[:, 0] == 1][:, 4] > 64).any() and (groups[groups[:, 0] == 1][:, 4] <= 64).any()
+    x, y0 = inst.inputs(0)
+    ws = inst.workspace(call)
+    stream = torch.cuda.current_stream().cuda_stream
+    _lib.timing_enable(True)
+    y = y0.clone()
+    inst.apply(call, x, y, ws)
+    _lib.timing_enable(False)
+    names, _ = _lib.timing_read_all()
+    assert names == ["mixed_fused"], names
+    assert _lib.workspace_status(ws.data_ptr(), stream) == 0
+    ref, _ = oracle_ref(wl, 0)
+    margin_line("mixed call in one launch, all rows",
+                check_close(y.cpu().numpy().view(np.uint16), ref, wl.dtype, "mixed one launch"))
+    first = y.cpu().numpy().view(np.uint16).copy()
+    y = y0.clone()
+    inst.apply(call, x, y, ws)
+    assert _lib.workspace_status(ws.data_ptr(), stream) == 0
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), first)
+    inst.close()
+
+
 @pytest.mark.parametrize("policy", [1, 2], ids=["mbgmv", "sgmv"])
 def test_wait_giveup_is_sticky_and_cleared(rt, decode7b, policy):
     """The fused launch's bounded wait (decode v for MBGMV, a tile's partial-sum flags for
