@@ -34,7 +34,9 @@
 // never wait, so every wait ends; the poll is bounded all the same, and a give-up is
 // recorded in the workspace header. One launch instead of two removes the drain of
 // the shrink grid before the expand grid can start. slora_shrink / slora_expand keep
-// the two separate kernels.
+// the two separate kernels. A call that also has decode groups runs them in the same
+// launch (mixed_fused_kernel, with the MBGMV bodies of mbgmv_dev.h): every shrink item
+// of both families first, then every expand item.
 #include <algorithm>
 
 #include <map>
