@@ -72,14 +72,28 @@ def algorithmic(wl, proj, call):
     # both families in one launch (a call with decode groups and segments in one launch)
     out["mixed_fused"] = {k: out["mbgmv_fused"][k] + out["sgmv_fused"][k]
                           for k in ("bytes", "flops", "tokens", "adapters")}
+    for f in ("sgmv_shrink", "sgmv_expand", "sgmv_fused", "mixed_fused"):
+        out[f]["mfma_flops"] = out["sgmv_" + f.split("_")[1] if f.startswith("sgmv") else "sgmv_fused"]["flops"]
     return out
+
+
+def projection_groups(wl, multi):
+    """Projections one step applies together: with multi, runs of consecutive projections
+    of one shape (one slora_apply_multi each); otherwise one projection per call."""
+    groups = []
+    for p, pr in enumerate(wl.projections):
+        if multi and groups and (wl.projections[groups[-1][0]].d_in, wl.projections[groups[-1][0]].d_out) == (pr.d_in, pr.d_out):
+            groups[-1].append(p)
+        else:
+            groups.append([p])
+    return groups
 
 
 # Source files each kernel family is compiled from (a counter summary is void once they change).
 KERNEL_SOURCES = {
     fam: [f"heterogeneous_lora_amd/csrc/{src}.hip", "heterogeneous_lora_amd/csrc/mbgmv_dev.h",
           "heterogeneous_lora_amd/csrc/device_common.h", "heterogeneous_lora_amd/csrc/internal.h"]
-    for fam, src in (("mbgmv", "mbgmv"), ("sgmv", "sgmv"), ("mixed", "sgmv"))
+    for fam, src in (("mbgmv", "mbgmv"), ("sgmv", "sgmv"), ("mixed", "sgmv"), ("multi", "sgmv"))
 }
 
 
@@ -297,14 +311,17 @@ def pct(a, q):
 
 
 def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev, overlap_steps=0,
-                 variant="paged"):
-    """Time `steps` steps (one apply per projection, rotating over n_inst instances) after
-    `warmup` untimed ones. Returns the measured figures; exits non-zero if a fused call's
-    wait gave up in any of them (its results would not be valid)."""
+                 variant="paged", multi=True):
+    """Time `steps` steps (every projection applied once, rotating over n_inst instances)
+    after `warmup` untimed ones. multi (paged variant): projections of one shape go
+    through one slora_apply_multi, otherwise one slora_apply each. Returns the measured
+    figures; exits non-zero if a fused call's wait gave up in any of them (its results
+    would not be valid)."""
     import torch
     from heterogeneous_lora_amd import _lib, runtime
     T = wl.n_tokens
     n_proj = len(wl.projections)
+    groups = projection_groups(wl, multi and variant != "gathered")
     active = [int(a) for a in wl.active_adapters()]
     log(f"[bench] {wl.name}: {wl.description}")
     log(f"[bench] {T} tokens, {len(active)} active adapters, {n_proj} projection(s), {n_inst} instance(s)")
@@ -319,8 +336,12 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
         fetch_ms.append(inst.fetch_ms)
         calls = [inst.call(p, policy) for p in range(n_proj)]
         io = [(runtime._dev_i16(x, inst.device), runtime._dev_i16(y0, inst.device)) for x, y0 in host_io]
-        wsize = _lib.gathered_workspace_size if variant == "gathered" else _lib.workspace_size
-        ws = torch.zeros(max(wsize(c) for c in calls), dtype=torch.uint8, device=dev)
+        if variant == "gathered":
+            need = max(_lib.gathered_workspace_size(c) for c in calls)
+        else:
+            need = max(_lib.workspace_size_multi([calls[p] for p in g]) if len(g) > 1
+                       else _lib.workspace_size(calls[g[0]]) for g in groups)
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
         insts.append((inst, calls, io, ws))
         log(f"[bench] instance {i} ready (fetch {inst.fetch_ms:.2f} ms)")
     del host_io
@@ -330,8 +351,10 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     fetch_bytes = sum(int(wl.ranks[a]) * (p.d_in + p.d_out) * 2 for a in active for p in wl.projections)
 
     stream = torch.cuda.current_stream(dev)
-    bound = [[inst.bind_apply(calls[p], io[p][0], io[p][1], ws, stream, gathered=variant == "gathered")
-              for p in range(n_proj)] for inst, calls, io, ws in insts]
+    bound = [[inst.bind_apply_multi([calls[p] for p in g], [io[p][0] for p in g], [io[p][1] for p in g],
+                                    ws, stream) if len(g) > 1 else
+              inst.bind_apply(calls[g[0]], io[g[0]][0], io[g[0]][1], ws, stream, gathered=variant == "gathered")
+              for g in groups] for inst, calls, io, ws in insts]
 
     def step(i):
         for run in bound[i % len(bound)]:
@@ -412,21 +435,32 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     value = T * steps / wall
     log(f"[bench] {steps} steps in {wall:.4f} s: {ms_per_step * 1e3:.1f} us/step, {value:.4g} tokens/s")
     alg = [algorithmic(wl, p, insts[0][1][p]) for p in range(n_proj)]
+    # algorithmic work per timed interval of each kernel id: one per projection, except a
+    # slora_apply_multi's, which covers its group of projections (both families)
+    per = {}
+    for g in groups:
+        if len(g) > 1:
+            fam = [sum(alg[p][f][q] for p in g for f in ("mbgmv_fused", "sgmv_fused")) for q in ("bytes", "flops")]
+            per.setdefault("multi_fused", []).append(fam + [sum(alg[p]["sgmv_fused"]["flops"] for p in g)])
+        else:
+            for k, a in alg[g[0]].items():
+                per.setdefault(k, []).append([a["bytes"], a["flops"], a.get("mfma_flops", 0)])
     kernels = {}
     for k in sorted(set(names)):
         d = np.array([m for n, m in zip(names, ms) if n == k])
         dp = np.array([m for n, m in zip(pnames, pms) if n == k]) * 1e3
         # the paged kernels' algorithmic work; the gathered variant's copy and its padded
         # products have no such figure of their own (0)
-        per_launch_bytes = float(np.mean([a[k]["bytes"] if variant == "paged" and k in a else 0 for a in alg]))
-        per_launch_flops = float(np.mean([a[k]["flops"] if variant == "paged" and k in a else 0 for a in alg]))
+        work = np.mean(per[k], axis=0) if variant == "paged" and k in per else np.zeros(3)
+        per_launch_bytes, per_launch_flops, mfma_flops = (float(v) for v in work)
         avg_s = float(d.mean()) * 1e-3
         kernels[k] = {"launches": int(d.size), "avg_us": round(avg_s * 1e6, 3),
                       "p10_us": pct(dp, 10), "p50_us": pct(dp, 50), "p90_us": pct(dp, 90),
                       "pct_launches": int(dp.size),
                       "algorithmic_bytes": int(per_launch_bytes),
                       "gbps": round(per_launch_bytes / avg_s / 1e9, 1),
-                      "tflops": round(per_launch_flops / avg_s / 1e12, 3)}
+                      "tflops": round(per_launch_flops / avg_s / 1e12, 3),
+                      "mfma_tflops": round(mfma_flops / avg_s / 1e12, 3)}
     n_timed = (steps + ev - 1) // ev
     kern_total_s = float(np.sum(ms)) * 1e-3 / n_timed
     step_bytes = sum(kv["algorithmic_bytes"] * kv["launches"] for kv in kernels.values()) / n_timed
@@ -520,9 +554,9 @@ def roofline_of(kernels, workload, kernel=None):
     r = {"bound": "hbm", "kernel": dom, "achieved": dk["gbps"], "peak": HBM_PEAK_GBPS,
          "unit": "GB/s", "frac": round(dk["gbps"] / HBM_PEAK_GBPS, 4),
          "traffic": load_traffic(dom, workload)}
-    if dom.startswith("sgmv"):
-        r["mfma_tflops"] = dk["tflops"]
-        r["mfma_frac"] = round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
+    if dk.get("mfma_tflops"):  # the segment (matrix-core) part of the kernel's work
+        r["mfma_tflops"] = dk["mfma_tflops"]
+        r["mfma_frac"] = round(dk["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
     return r
 
 
@@ -542,6 +576,9 @@ def main():
                     help="decode_7b only: skip the prefill_sgmv sub-record")
     ap.add_argument("--pct-steps", type=int, default=64,
                     help="extra steps, every launch timed, for the p10/p50/p90 kernel durations")
+    ap.add_argument("--per-projection", action="store_true",
+                    help="one slora_apply per projection, instead of one slora_apply_multi per "
+                         "run of same-shape projections")
     ap.add_argument("--variant", default="paged", choices=["paged", "gathered", "split"],
                     help="paged: slora_apply on the unified pool; gathered: slora_apply_gathered "
                          "(adapters copied out and padded, then a padded batched GEMM); split: "
@@ -589,7 +626,7 @@ def main():
     log(f"[bench] device: {dinfo}")
     main_run = run_workload(wl, policy, args.instances, args.steps, args.warmup, args.event_every,
                             args.pct_steps, dev, overlap_steps=args.overlap_steps if args.variant == "paged" else 0,
-                            variant=args.variant)
+                            variant=args.variant, multi=not args.per_projection)
     roofline = roofline_of(main_run["kernels"], wl.name)
     copy_ref = copy_reference(dev)
     roofline["copy_gbps"] = copy_ref["gbps"]
@@ -605,14 +642,13 @@ def main():
     if args.config == "decode_7b" and not args.no_prefill and args.variant == "paged":
         pw = workloads.make("prefill_sgmv")
         pr = run_workload(pw, 0, 2, max(10, min(args.steps, 40)), max(2, min(args.warmup, 5)),
-                          args.event_every, min(args.pct_steps, 16), dev)
+                          args.event_every, min(args.pct_steps, 16), dev, multi=not args.per_projection)
         prefill = {"workload": pw.name, "value": round(pr["value"], 1), "unit": "tokens/s",
                    "ms_per_step": round(pr["ms_per_step"], 5), "tokens": pw.n_tokens,
                    "projections": len(pw.projections), "instances_rotated": 2,
                    "kernels": pr["kernels"], "step_kernel_us": pr["step_kernel_us"],
                    "step_algorithmic_gbps": pr["step_algorithmic_gbps"],
-                   "roofline": {k: roofline_of(pr["kernels"], pw.name, k)
-                                for k in ("sgmv_fused",) if k in pr["kernels"]},
+                   "roofline": {k: roofline_of(pr["kernels"], pw.name, k) for k in pr["kernels"]},
                    "workspace_status": pr["workspace_status"]}
 
     cpu = None
@@ -631,6 +667,8 @@ def main():
                    "shape": [[p.d_in, p.d_out] for p in wl.projections],
                    "active_adapters": main_run["active"], "policy": args.policy,
                    "variant": args.variant,
+                   "projection_calls": "per projection" if args.per_projection else
+                                       "one slora_apply_multi per run of same-shape projections",
                    "instances_rotated": args.instances, "accumulate": "f32",
                    "page_elems": wl.page_elems, "pool_pages": wl.n_pages},
         "roofline": roofline,

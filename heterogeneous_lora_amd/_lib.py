@@ -105,6 +105,8 @@ def load(path: str = LIB_PATH):
         "slora_expand": ([P, P, P, P, P, _c_i64, P], I),
         "slora_apply": ([P, P, P, P, P, _c_i64, P], I),
         "slora_apply_noalloc": ([P, P, P, P, P], I),
+        "slora_workspace_size_multi": ([I, P, P, P], I),
+        "slora_apply_multi": ([I, P, P, P, P, P, _c_i64, P], I),
         "slora_gathered_workspace_size": ([P, P, P], I),
         "slora_apply_gathered": ([P, P, P, P, P, _c_i64, P], I),
         "slora_pool_create_ordered": ([P, _c_i64, I, I, P], I),
@@ -431,6 +433,50 @@ def apply_noalloc(call: Call, x: int, y: int, stream: int):
                                       _vp(y), _vp(stream)), "apply_noalloc")
 
 
+class MultiCall:
+    """Host-side arguments of one slora_apply_multi: the projections' Call objects (their
+    lora structs side by side, the routing of the first) and the x / y pointers."""
+
+    def __init__(self, calls: Sequence[Call], xs: Sequence[int], ys: Sequence[int]):
+        self.calls = list(calls)
+        self.n = len(self.calls)
+        self.loras = (Lora * max(self.n, 1))(*[c.lora for c in self.calls])
+        self.xs = (_vp * max(self.n, 1))(*xs)
+        self.ys = (_vp * max(self.n, 1))(*ys)
+
+
+def workspace_size_multi(calls: Sequence[Call]) -> int:
+    m = MultiCall(calls, [0] * len(calls), [0] * len(calls))
+    n = _c_i64()
+    _check(load().slora_workspace_size_multi(m.n, m.loras, ctypes.byref(calls[0].routing),
+                                             ctypes.byref(n)), "workspace_size_multi")
+    return n.value
+
+
+def apply_multi(calls: Sequence[Call], xs: Sequence[int], ys: Sequence[int], ws: int, ws_bytes: int,
+                stream: int):
+    m = MultiCall(calls, xs, ys)
+    _check(load().slora_apply_multi(m.n, m.loras, ctypes.byref(m.calls[0].routing), m.xs, m.ys,
+                                    _vp(ws), ws_bytes, _vp(stream)), "apply_multi")
+
+
+def bind_apply_multi(calls: Sequence[Call], xs: Sequence[int], ys: Sequence[int], ws: int,
+                     ws_bytes: int, stream: int):
+    """slora_apply_multi with its arguments converted once (see bind_apply)."""
+    m = MultiCall(calls, xs, ys)
+    f = load().slora_apply_multi
+    args = (m.n, m.loras, ctypes.byref(m.calls[0].routing), m.xs, m.ys, _vp(ws), _c_i64(ws_bytes),
+            _vp(stream))
+
+    def run():
+        rc = f(*args)
+        if rc != OK:
+            _check(rc, "apply_multi")
+
+    run.call = m
+    return run
+
+
 def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int,
                gathered: bool = False):
     """slora_apply (or slora_apply_gathered) with its arguments converted once: returns a
@@ -450,7 +496,7 @@ def bind_apply(call: Call, x: int, y: int, ws: int, ws_bytes: int, stream: int,
 
 
 KERNELS = ["mbgmv_shrink", "mbgmv_expand", "sgmv_shrink", "sgmv_expand", "mbgmv_fused", "gather",
-           "fetch", "sgmv_fused", "mixed_fused"]
+           "fetch", "sgmv_fused", "mixed_fused", "multi_fused"]
 
 
 def timing_enable(on: bool):

@@ -412,6 +412,125 @@ int launch_plan(const slora_lora* L, const slora_routing* R, const PlanView& pv,
   return SLORA_OK;
 }
 
+// ---------------------------------------------------------------- several projections
+// Projections that can share one plan: the same pool, geometry and adapters, with the
+// same page-table layout (base, rank and scale arrays equal; each its own table).
+int same_layout(const slora_lora* a, const slora_lora* b, int32_t p) {
+  if (b->pool != a->pool || b->n_pages != a->n_pages || b->page_elems != a->page_elems ||
+      b->dtype != a->dtype || b->d_in != a->d_in || b->d_out != a->d_out ||
+      b->n_adapters != a->n_adapters || b->r_max != a->r_max ||
+      b->page_table_len != a->page_table_len || (b->page_table_len > 0 && !b->page_table))
+    return fail(SLORA_E_INVALID, "apply_multi: projection %d differs from projection 0 in pool, "
+                "geometry or adapters", p);
+  const size_t n = (size_t)std::max<int32_t>(a->n_adapters, 0);
+  if (n && (!b->base || !b->rank || !b->scale || memcmp(a->base, b->base, n * sizeof *a->base) ||
+            memcmp(a->rank, b->rank, n * sizeof *a->rank) || memcmp(a->scale, b->scale, n * sizeof *a->scale)))
+    return fail(SLORA_E_INVALID, "apply_multi: projection %d's base / rank / scale differ from "
+                "projection 0's", p);
+  return SLORA_OK;
+}
+
+int64_t multi_region(const slora_lora* L, const slora_routing* R) {
+  return (ws_layout(L, R).total + 255) / 256 * 256;
+}
+
+// The launches of a planned call over n projections; projection p's workspace region
+// starts at ws + p * region.
+int launch_multi(int32_t n, const slora_lora* Ls, const slora_routing* R, const PlanView& pv,
+                 const void* const* xs, void* const* ys, void* ws, int64_t region,
+                 const WsLayout& lay, hipStream_t s, Ring* ring) {
+  const slora_lora* L = &Ls[0];
+  uint8_t* wsb = (uint8_t*)ws;
+  Geom g;
+  g.pool = (const uint16_t*)L->pool;
+  g.n_pages = L->n_pages;
+  g.P = L->page_elems;
+  g.dtype = L->dtype;
+  g.d_in = L->d_in;
+  g.d_out = L->d_out;
+  g.cA = (L->d_in + g.P - 1) / g.P;
+  g.cB = (L->d_out + g.P - 1) / g.P;
+  g.pt = L->page_table;
+  g.r_max = L->r_max;
+  unsigned long long* err = (unsigned long long*)wsb;
+  uint32_t& last = g_ws_tag[ws];
+  if (last == 0xFFFFFFFFu) {  // as in launch_plan, over every projection's region
+    const hipError_t e = launch_zero(wsb + kHeaderBytes, n * region - kHeaderBytes, s);
+    if (e != hipSuccess) return hip_fail(e, "workspace clear");
+    last = 0;
+  }
+  const uint32_t tag = ++last;
+  int rc = order_fused(*ring, s);
+  if (rc) return rc;
+  const int32_t v_stride = sg_v_stride(L->r_max);
+  const SgSplit sp = pv.n_sg ? sg_split(L->d_in, pv.n_sg, sgmv_shrink_resident(pv.sg_max_rank, L->dtype))
+                             : SgSplit{};
+  const int64_t part_stride = (int64_t)R->n_tokens * v_stride;
+  ProjIO io[kMaxProj], io2[kMaxProj];
+  int32_t hi = 0;
+  while (hi < pv.n_sg && pv.sg[hi].rank > 64) ++hi;
+  const bool split = hi >= kSgSplitTiles && pv.n_sg - hi >= kSgSplitTiles;
+  for (int32_t p = 0; p < n; ++p) {
+    uint8_t* r = wsb + p * region;
+    io[p] = ProjIO{Ls[p].page_table, xs[p], ys[p], r + lay.v_off, (float*)(r + lay.sg_off),
+                   (uint32_t*)(r + lay.flg_off)};
+    io2[p] = io[p];
+    io2[p].flags += 2 * (int64_t)hi * sp.ksplit;  // past every flag the wide tiles can use
+  }
+  const hipError_t e = timed_launch(SLORA_K_MULTI_FUSED, s, [&](const LaunchEvents& le) {
+    if (!split)
+      return launch_multi_fused(g, pv.tok, pv.sg, pv.n_sg, pv.sg_max_rank, sp.ksplit, sp.kc, v_stride,
+                                part_stride, io, n, tag, g_spin_limit, err, s, le, pv.mb, pv.n_mb,
+                                pv.n_mb_shrink, pv.mb_max_tok);
+    // the rank classes in two launches (as launch_plan does), the decode groups with the
+    // narrower one; timed as one interval
+    LaunchEvents first = le, second = le;
+    first.stop = nullptr;
+    second.start = nullptr;
+    const hipError_t e1 = launch_multi_fused(g, pv.tok, pv.sg, hi, pv.sg_max_rank, sp.ksplit, sp.kc,
+                                             v_stride, part_stride, io, n, tag, g_spin_limit, err, s,
+                                             first, nullptr, 0, 0, 0);
+    if (e1 != hipSuccess) return e1;
+    return launch_multi_fused(g, pv.tok, pv.sg + hi, pv.n_sg - hi, pv.sg[hi].rank, sp.ksplit, sp.kc,
+                              v_stride, part_stride, io2, n, tag, g_spin_limit, err, s, second, pv.mb,
+                              pv.n_mb, pv.n_mb_shrink, pv.mb_max_tok);
+  });
+  return e != hipSuccess ? hip_fail(e, "multi-projection launch") : SLORA_OK;
+}
+
+int run_multi(int32_t n, const slora_lora* Ls, const slora_routing* R, const void* const* xs,
+              void* const* ys, void* ws, int64_t ws_bytes, void* stream) {
+  clear_error();
+  if (n < 1 || n > kMaxProj) return fail(SLORA_E_INVALID, "apply_multi: %d projections (1..%d)", n, kMaxProj);
+  if (!Ls || !xs || !ys) return fail(SLORA_E_INVALID, "apply_multi: NULL argument");
+  PlanView pv;
+  const int64_t bytes = plan_bytes(&Ls[0], R, &t_scratch, &pv);
+  if (bytes < 0) return (int)bytes;
+  for (int32_t p = 1; p < n; ++p) {
+    const int rc = same_layout(&Ls[0], &Ls[p], p);
+    if (rc) return rc;
+  }
+  for (int32_t p = 0; p < n; ++p)
+    if (!xs[p] || !ys[p] || misaligned(xs[p], 16) || misaligned(ys[p], 16))
+      return fail(SLORA_E_INVALID, "apply_multi: x / y of projection %d must be 16-byte aligned device pointers", p);
+  const WsLayout lay = ws_layout(&Ls[0], R);
+  const int64_t region = multi_region(&Ls[0], R);
+  if (!ws || misaligned(ws, 256)) return fail(SLORA_E_INVALID, "ws must be 256-byte aligned");
+  if (ws_bytes < n * region)
+    return fail(SLORA_E_INVALID, "workspace of %lld bytes is smaller than the %lld needed",
+                (long long)ws_bytes, (long long)(n * region));
+  if (pv.n_routed == 0) return SLORA_OK;
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipStream_t s = (hipStream_t)stream;
+  SlotRef slot;
+  int rc = acquire_slot((size_t)bytes, s, true, &slot);
+  if (rc) return rc;
+  plan_write(&Ls[0], R, &t_scratch, slot.host(), &pv);
+  rc = launch_multi(n, Ls, R, pv, xs, ys, ws, region, lay, s, slot.ring);
+  const int rc2 = release_slot(slot, s, rc == SLORA_OK);
+  return rc ? rc : rc2;
+}
+
 }  // namespace
 
 namespace {
@@ -640,6 +759,15 @@ static int impl_slora_workspace_size(const slora_lora* lora, const slora_routing
   return SLORA_OK;
 }
 
+static int impl_slora_workspace_size_multi(int32_t n, const slora_lora* loras,
+                                           const slora_routing* routing, int64_t* bytes) {
+  clear_error();
+  if (!loras || !routing || !bytes) return fail(SLORA_E_INVALID, "workspace_size_multi: NULL argument");
+  if (n < 1 || n > kMaxProj) return fail(SLORA_E_INVALID, "workspace_size_multi: %d projections (1..%d)", n, kMaxProj);
+  *bytes = n * multi_region(&loras[0], routing);
+  return SLORA_OK;
+}
+
 static int impl_slora_workspace_status(void* ws, void* stream, int32_t* status) {
   clear_error();
   if (!status) return fail(SLORA_E_INVALID, "workspace_status: status is NULL");
@@ -783,6 +911,17 @@ int slora_expand(const slora_lora* lora, const slora_routing* routing, const flo
 int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
                 void* ws, int64_t ws_bytes, void* stream) {
   return slora::guarded(__func__, [&] { return impl_slora_apply(lora, routing, x, y, ws, ws_bytes, stream); });
+}
+
+int slora_workspace_size_multi(int32_t n_proj, const slora_lora* loras, const slora_routing* routing,
+                               int64_t* bytes) {
+  return slora::guarded(__func__, [&] { return impl_slora_workspace_size_multi(n_proj, loras, routing, bytes); });
+}
+
+int slora_apply_multi(int32_t n_proj, const slora_lora* loras, const slora_routing* routing,
+                      const void* const* xs, void* const* ys, void* ws, int64_t ws_bytes,
+                      void* stream) {
+  return slora::guarded(__func__, [&] { return run_multi(n_proj, loras, routing, xs, ys, ws, ws_bytes, stream); });
 }
 
 int slora_plan_inspect(const slora_lora* lora, const slora_routing* routing, int32_t* n_groups,

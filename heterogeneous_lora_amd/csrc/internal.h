@@ -202,6 +202,30 @@ hipError_t launch_sgmv_fused(const Geom& g, const int32_t* tok, const SgTile* ti
                              const MbItem* mb_items = nullptr, int32_t n_mb = 0,
                              int32_t n_mb_shrink = 0, int32_t mb_max_tok = 0, void* v_mb = nullptr);
 
+// One projection of a launch over several projections of one batch: its page table, x,
+// y (holding y0) and its workspace region's MBGMV v, segment partial sums and flags.
+constexpr int kMaxProj = 8;
+struct ProjIO {
+  const int32_t* pt;
+  const void* x;
+  void* y;
+  void* v_mb;
+  float* vpart;
+  uint32_t* flags;
+};
+
+// The apply of n_proj projections (shared plan: the same routing, ranks and page-table
+// layout, one ProjIO each) in one launch: MBGMV items and segment tiles of every
+// projection, every shrink item before every expand item. err: the give-up word of the
+// first projection's workspace region. Tiles in descending rank, as launch_sgmv_fused.
+hipError_t launch_multi_fused(const Geom& g, const int32_t* tok, const SgTile* tiles,
+                              int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
+                              int32_t v_stride, int64_t split_stride, const ProjIO* io,
+                              int32_t n_proj, uint32_t tag, int32_t spin_limit,
+                              unsigned long long* err, hipStream_t s, const LaunchEvents& ev,
+                              const MbItem* mb_items, int32_t n_mb, int32_t n_mb_shrink,
+                              int32_t mb_max_tok);
+
 // Ablation baseline: copy each request's adapter out of the pool into contiguous,
 // rank-padded memory (gather.hip). One entry per request.
 struct GatherReq {

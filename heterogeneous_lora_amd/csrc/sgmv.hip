@@ -644,41 +644,57 @@ __global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void sgmv_fused
   else sg_expand_item<DT, NBM, KBM>(g, w, tag, spin_limit, err, y, L - n_shrink, lds);
 }
 
-// ------------------------------------------------------------------ both families (apply calls)
+// ------------------------------------------------------------------ both families, several projections
 // A call with decode groups (MBGMV items) and segment tiles runs both families in one
 // launch, so that one family's ramp and tail overlap the other's work and the stream
-// has one launch instead of two: workgroups [MBGMV shrink items][segment shrink items]
-// [MBGMV expand items][segment expand items]. Every shrink item of either family comes
-// before every expand item and none waits, so the in-order-dispatch argument holds for
-// both hand-offs (v words for MBGMV, flags for the segments); they share the call's tag
-// and the workspace header's give-up word. LDS is the larger of the two families' needs.
+// has one launch instead of two; a call over several projections of one batch (same
+// routing and adapters, one page table, x, y and workspace region each) runs all of
+// them in that launch too. Workgroups: [MBGMV shrink items][segment shrink items]
+// [MBGMV expand items][segment expand items], each part projection-major. Every shrink
+// item of either family and any projection comes before every expand item and none
+// waits, so the in-order-dispatch argument holds for every hand-off (v words for
+// MBGMV, flags for the segments, each in its projection's workspace region); they
+// share the call's tag and the first region's give-up word. LDS is the larger of the
+// two families' needs.
+struct Projs {
+  ProjIO p[kMaxProj];
+};
+
 template <int DT, bool kUniformChunk, int NBM, int KBM>
 __global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void mixed_fused_kernel(
     Geom g, SgWork w, const MbItem* __restrict__ items, int32_t n_mb, int32_t n_mb_shrink,
-    const uint16_t* __restrict__ x, void* v_mb, uint32_t tag, int32_t spin_limit,
-    unsigned long long* err, uint16_t* __restrict__ y) {
+    Projs pr, int32_t n_proj, uint32_t tag, int32_t spin_limit, unsigned long long* err) {
   constexpr int kMbBytes = mb::kRedBytes > kMbGroup * mb::kBatchVecs * 16 ? mb::kRedBytes : kMbGroup * mb::kBatchVecs * 16;
   constexpr int kBytes = fused_lds_bytes(NBM, KBM) > kMbBytes ? fused_lds_bytes(NBM, KBM) : kMbBytes;
   __shared__ uint4 lds[(kBytes + 15) / 16];
-  int L = (int)blockIdx.x;
-  if (L < n_mb_shrink) {
-    const MbItem it = items[L];
-    mb::run_item<DT, kUniformChunk, true>(g, it, x, v_mb, y, tag, err, spin_limit, lds);
+  const int a = n_mb_shrink, b = sg_shrink_items<NBM, KBM>(w), c = n_mb - n_mb_shrink;
+  int L = (int)blockIdx.x, part, p, i;
+  if (L < n_proj * a) {
+    part = 0, p = L / a, i = L % a;
+  } else if ((L -= n_proj * a) < n_proj * b) {
+    part = 1, p = L / b, i = L % b;
+  } else if ((L -= n_proj * b) < n_proj * c) {
+    part = 2, p = L / c, i = L % c;
+  } else {
+    L -= n_proj * c;
+    const int d = w.n_tiles * sg_expand_blocks(g);
+    part = 3, p = L / d, i = L % d;
+  }
+  const ProjIO io = pr.p[p];
+  Geom gp = g;
+  gp.pt = io.pt;
+  const uint16_t* x = static_cast<const uint16_t*>(io.x);
+  uint16_t* y = static_cast<uint16_t*>(io.y);
+  if (part == 0 || part == 2) {
+    const MbItem it = items[part == 0 ? i : a + i];
+    mb::run_item<DT, kUniformChunk, true>(gp, it, x, io.v_mb, y, tag, err, spin_limit, lds);
     return;
   }
-  L -= n_mb_shrink;
-  const int sg_shrink = sg_shrink_items<NBM, KBM>(w);
-  if (L < sg_shrink) {
-    sg_shrink_item<DT, NBM, KBM>(g, w, x, tag, L, lds);
-    return;
-  }
-  L -= sg_shrink;
-  if (L < n_mb - n_mb_shrink) {
-    const MbItem it = items[n_mb_shrink + L];
-    mb::run_item<DT, kUniformChunk, true>(g, it, x, v_mb, y, tag, err, spin_limit, lds);
-    return;
-  }
-  sg_expand_item<DT, NBM, KBM>(g, w, tag, spin_limit, err, y, L - (n_mb - n_mb_shrink), lds);
+  SgWork wp = w;
+  wp.vpart = io.vpart;
+  wp.flags = io.flags;
+  if (part == 1) sg_shrink_item<DT, NBM, KBM>(gp, wp, x, tag, i, lds);
+  else sg_expand_item<DT, NBM, KBM>(gp, wp, tag, spin_limit, err, y, i, lds);
 }
 
 template <int DT>
@@ -713,51 +729,54 @@ hipError_t expand_dt(const Geom& g, const int32_t* tok, const SgTile* tiles, int
 }
 
 // Both launchers: the grid, the segment work and, for a launch of both families, the
-// MBGMV items (n_mb = 0: segments only).
+// MBGMV items (n_mb = 0: segments only), for n_proj projections.
 struct MbPart {
   const MbItem* items;
   int32_t n_mb, n_mb_shrink;
-  void* v;
 };
 
 template <int DT, int NBM, int KBM>
-hipError_t fused_launch(const Geom& g, const SgWork& w, const MbPart& mp, const void* x,
-                        uint32_t tag, int32_t spin_limit, unsigned long long* err, void* y,
+hipError_t fused_launch(const Geom& g, const SgWork& w, const MbPart& mp, const Projs& pr,
+                        int32_t n_proj, uint32_t tag, int32_t spin_limit, unsigned long long* err,
                         hipStream_t s, const LaunchEvents& ev) {
   const int per_wg = kSubPasses * kCols;
   const int64_t ncb = (g.d_out + per_wg - 1) / per_wg;
   const int64_t wide = NBM == 4 && KBM == 4 ? w.n_wide : 0;
-  const int64_t n = (int64_t)(w.n_tiles + wide) * w.ksplit + (int64_t)w.n_tiles * ncb + mp.n_mb;
+  const int64_t n = ((int64_t)(w.n_tiles + wide) * w.ksplit + (int64_t)w.n_tiles * ncb + mp.n_mb) * n_proj;
   if (n > INT32_MAX) return hipErrorInvalidValue;
-  const uint16_t* xp = (const uint16_t*)x;
-  uint16_t* yp = (uint16_t*)y;
-  if (mp.n_mb == 0) {
+  if (n == 0) return hipSuccess;
+  if (mp.n_mb == 0 && n_proj == 1) {
+    const ProjIO& io = pr.p[0];
     hipExtLaunchKernelGGL((sgmv_fused_kernel<DT, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
                           ev.start, ev.stop, 0, g, w.tiles, w.tok, w.kc, w.ksplit, w.n_tiles, w.n_wide,
-                          xp, w.vpart, w.v_stride, w.split_stride, w.flags, tag, spin_limit, err, yp);
+                          (const uint16_t*)io.x, io.vpart, w.v_stride, w.split_stride, io.flags, tag,
+                          spin_limit, err, (uint16_t*)io.y);
     return hipGetLastError();
   }
   if constexpr (NBM == 8) {
-    return hipErrorInvalidValue;  // both families take the 3-per-CU wide template
-  } else if (g.P % 512 == 0)
+    if (mp.n_mb > 0) return hipErrorInvalidValue;  // both families take the 3-per-CU wide template
     hipExtLaunchKernelGGL((mixed_fused_kernel<DT, true, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
-                          ev.start, ev.stop, 0, g, w, mp.items, mp.n_mb, mp.n_mb_shrink, xp, mp.v, tag,
-                          spin_limit, err, yp);
-  else
+                          ev.start, ev.stop, 0, g, w, mp.items, 0, 0, pr, n_proj, tag, spin_limit, err);
+  } else if (g.P % 512 == 0) {
+    hipExtLaunchKernelGGL((mixed_fused_kernel<DT, true, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
+                          ev.start, ev.stop, 0, g, w, mp.items, mp.n_mb, mp.n_mb_shrink, pr, n_proj, tag,
+                          spin_limit, err);
+  } else {
     hipExtLaunchKernelGGL((mixed_fused_kernel<DT, false, NBM, KBM>), dim3((unsigned)n), dim3(64 * kWaves), 0, s,
-                          ev.start, ev.stop, 0, g, w, mp.items, mp.n_mb, mp.n_mb_shrink, xp, mp.v, tag,
-                          spin_limit, err, yp);
+                          ev.start, ev.stop, 0, g, w, mp.items, mp.n_mb, mp.n_mb_shrink, pr, n_proj, tag,
+                          spin_limit, err);
+  }
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t fused_dt(const Geom& g, SgWork w, int32_t max_rank, const MbPart& mp, const void* x,
-                    uint32_t tag, int32_t spin_limit, unsigned long long* err, void* y,
+hipError_t fused_dt(const Geom& g, SgWork w, int32_t max_rank, const MbPart& mp, const Projs& pr,
+                    int32_t n_proj, uint32_t tag, int32_t spin_limit, unsigned long long* err,
                     hipStream_t s, const LaunchEvents& ev) {
   w.n_wide = 0;
-  if (max_rank <= 16) return fused_launch<DT, 1, 1>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
-  if (max_rank <= 32) return fused_launch<DT, 2, 1>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
-  if (max_rank <= 64) return fused_launch<DT, 4, 2>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
+  if (max_rank <= 16) return fused_launch<DT, 1, 1>(g, w, mp, pr, n_proj, tag, spin_limit, err, s, ev);
+  if (max_rank <= 32) return fused_launch<DT, 2, 1>(g, w, mp, pr, n_proj, tag, spin_limit, err, s, ev);
+  if (max_rank <= 64) return fused_launch<DT, 4, 2>(g, w, mp, pr, n_proj, tag, spin_limit, err, s, ev);
   // ranks above 64: the tiles that have them come first (descending rank; the tile
   // records are in host-visible pinned memory). Beside narrower tiles they are shrunk in
   // two 64-row blocks, so that the whole launch keeps 3 workgroups per CU; a launch of
@@ -766,11 +785,40 @@ hipError_t fused_dt(const Geom& g, SgWork w, int32_t max_rank, const MbPart& mp,
   for (int32_t i = w.n_wide; i < w.n_tiles; ++i)
     if (w.tiles[i].rank > 64) return hipErrorInvalidValue;
   if (w.n_wide == w.n_tiles && mp.n_mb == 0)
-    return fused_launch<DT, 8, 4>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
-  return fused_launch<DT, 4, 4>(g, w, mp, x, tag, spin_limit, err, y, s, ev);
+    return fused_launch<DT, 8, 4>(g, w, mp, pr, n_proj, tag, spin_limit, err, s, ev);
+  return fused_launch<DT, 4, 4>(g, w, mp, pr, n_proj, tag, spin_limit, err, s, ev);
 }
 
 }  // namespace
+
+hipError_t launch_multi_fused(const Geom& g, const int32_t* tok, const SgTile* tiles,
+                              int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
+                              int32_t v_stride, int64_t split_stride, const ProjIO* io,
+                              int32_t n_proj, uint32_t tag, int32_t spin_limit,
+                              unsigned long long* err, hipStream_t s, const LaunchEvents& ev,
+                              const MbItem* mb_items, int32_t n_mb, int32_t n_mb_shrink,
+                              int32_t mb_max_tok) {
+  if (n_tiles < 0 || n_mb < 0 || n_mb_shrink < 0 || n_mb_shrink > n_mb || n_proj < 1 ||
+      n_proj > kMaxProj || !io || !err || tag == 0)
+    return hipErrorInvalidValue;
+  if (n_tiles > 0 && (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit ||
+                      kc % kRound || (v_stride & 3) || !tiles))
+    return hipErrorInvalidValue;
+  if (n_mb > 0 && (!mb_items || mb_max_tok < 1 || mb_max_tok > kMbGroup)) return hipErrorInvalidValue;
+  Projs pr{};
+  for (int32_t p = 0; p < n_proj; ++p) {
+    pr.p[p] = io[p];
+    if (!io[p].pt || !io[p].x || !io[p].y || (n_tiles > 0 && (!io[p].vpart || !io[p].flags)) ||
+        (n_mb > 0 && !io[p].v_mb))
+      return hipErrorInvalidValue;
+  }
+  const SgWork w{tiles, tok, kc, n_tiles > 0 ? ksplit : 1, n_tiles, 0, nullptr, v_stride, split_stride, nullptr};
+  const MbPart mp{mb_items, n_mb, n_mb_shrink};
+  const int32_t mr = n_tiles > 0 ? max_rank : 1;
+  return g.dtype == SLORA_F16
+             ? fused_dt<SLORA_F16>(g, w, mr, mp, pr, n_proj, tag, spin_limit, err, s, ev)
+             : fused_dt<SLORA_BF16>(g, w, mr, mp, pr, n_proj, tag, spin_limit, err, s, ev);
+}
 
 hipError_t launch_sgmv_fused(const Geom& g, const int32_t* tok, const SgTile* tiles,
                              int32_t n_tiles, int32_t max_rank, int32_t ksplit, int32_t kc,
@@ -780,17 +828,10 @@ hipError_t launch_sgmv_fused(const Geom& g, const int32_t* tok, const SgTile* ti
                              const LaunchEvents& ev, const MbItem* mb_items, int32_t n_mb,
                              int32_t n_mb_shrink, int32_t mb_max_tok, void* v_mb) {
   if (n_tiles <= 0) return hipSuccess;
-  if (max_rank < 1 || max_rank > kMaxRank || ksplit < 1 || ksplit > kSgMaxSplit || kc % kRound ||
-      (v_stride & 3) || !flags || !err || tag == 0)
-    return hipErrorInvalidValue;
-  if (n_mb < 0 || n_mb_shrink < 0 || n_mb_shrink > n_mb ||
-      (n_mb > 0 && (!mb_items || !v_mb || mb_max_tok < 1 || mb_max_tok > kMbGroup)))
-    return hipErrorInvalidValue;
-  const SgWork w{tiles, tok, kc, ksplit, n_tiles, 0, vpart, v_stride, split_stride, flags};
-  const MbPart mp{mb_items, n_mb, n_mb_shrink, v_mb};
-  return g.dtype == SLORA_F16
-             ? fused_dt<SLORA_F16>(g, w, max_rank, mp, x, tag, spin_limit, err, y, s, ev)
-             : fused_dt<SLORA_BF16>(g, w, max_rank, mp, x, tag, spin_limit, err, y, s, ev);
+  const ProjIO io{g.pt, x, y, v_mb, vpart, flags};
+  return launch_multi_fused(g, tok, tiles, n_tiles, max_rank, ksplit, kc, v_stride, split_stride,
+                            &io, 1, tag, spin_limit, err, s, ev, mb_items, n_mb, n_mb_shrink,
+                            mb_max_tok);
 }
 
 int sgmv_shrink_resident(int32_t max_rank, int32_t dtype) {

@@ -169,6 +169,17 @@ class PagedLoRA:
         return _lib.bind_apply(call, x.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(),
                                s.cuda_stream, gathered=gathered)
 
+    def multi_workspace(self, calls) -> torch.Tensor:
+        """Device workspace for apply_multi over `calls` (zero-filled once)."""
+        return torch.zeros(_lib.workspace_size_multi(calls), dtype=torch.uint8, device=self.device)
+
+    def bind_apply_multi(self, calls, xs, ys, ws: torch.Tensor,
+                         stream: Optional[torch.cuda.Stream] = None):
+        """slora_apply_multi over several projections' calls, marshalled once."""
+        s = stream or torch.cuda.current_stream(self.device)
+        return _lib.bind_apply_multi(calls, [x.data_ptr() for x in xs], [y.data_ptr() for y in ys],
+                                     ws.data_ptr(), ws.numel(), s.cuda_stream)
+
     def shrink(self, call, x, v, ws, stream=None):
         s = stream or torch.cuda.current_stream(self.device)
         _lib.shrink(call, x.data_ptr(), v.data_ptr(), ws.data_ptr(), ws.numel(), s.cuda_stream)

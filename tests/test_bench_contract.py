@@ -52,6 +52,7 @@ def test_bench_prints_one_json_line():
     assert d["device"]["compute_units"] > 0
     pf = d["prefill"]
     assert pf["workload"] == "prefill_sgmv" and pf["value"] > 0 and pf["workspace_status"] == "clean"
-    pr = pf["roofline"]["sgmv_fused"]
+    # the four projections in one slora_apply_multi per step
+    pr = pf["roofline"]["multi_fused"]
     assert pr["unit"] == "GB/s" and 0 < pr["frac"] < 1 and 0 < pr["mfma_frac"] < 1
-    assert set(pf["kernels"]) == {"sgmv_fused"}
+    assert set(pf["kernels"]) == {"multi_fused"}

@@ -213,6 +213,53 @@ MB_GROUP, SG_TILE = 4, 64
 AUTO_SGMV_TOK, AUTO_SGMV_BATCH, AUTO_MBGMV_MIN, AUTO_SGMV_SHARE = 4, 256, 128, 4
 
 
+def _multi_code(calls, ws_bytes=1 << 30, xs=None, ys=None):
+    n = len(calls)
+    try:
+        _lib.apply_multi(calls, xs or [FAKE_DEV] * n, ys or [FAKE_DEV] * n, FAKE_DEV, ws_bytes, 0)
+    except _lib.SloraError as e:
+        return e.code
+    return 0
+
+
+def test_apply_multi_validation():
+    """slora_apply_multi refuses, before anything runs, projections that cannot share one
+    plan (any field that fixes the plan differs, or the base / rank / scale arrays do),
+    a projection count outside 1..8, misaligned x / y and a workspace smaller than one
+    region per projection; its workspace is n regions of slora_workspace_size rounded
+    to 256 bytes."""
+    wl = workloads.random_small(3, n_tokens=20, n_segments=3, rank_choices=(4, 8))
+    call, pool, pt, base = _call(wl)
+    one = _lib.workspace_size(call)
+    for n in (1, 3, 8):
+        assert _lib.workspace_size_multi([call] * n) == n * ((one + 255) // 256 * 256)
+    with pytest.raises(_lib.SloraError):
+        _lib.workspace_size_multi([call] * 9)
+    assert _multi_code([call] * 9) == _lib.E_INVALID
+    assert _multi_code([call] * 2, ws_bytes=_lib.workspace_size_multi([call]) * 2 - 256) == _lib.E_INVALID
+    assert "workspace" in _lib.last_error()
+    assert _multi_code([call] * 2, xs=[FAKE_DEV, FAKE_DEV + 8]) == _lib.E_INVALID
+    differing = {
+        "d_out": dict(d_out=wl.projections[0].d_out + 8),
+        "dtype": dict(dtype="bf16" if wl.dtype == "f16" else "f16"),
+        "r_max": dict(r_max=int(wl.ranks.max()) + 1),
+        "page_table_len": dict(page_table_len=int(pt.size) + 1),
+        "pool": dict(pool_ptr=FAKE_DEV + 256),
+        "base": dict(base=np.where(base >= 0, base + 1, base)),
+        "scale": dict(scale=wl.scales * 2),
+    }
+    for name, over in differing.items():
+        c2, _, _, _ = _call(wl, pool=pool, **over)
+        assert _multi_code([call, c2]) == _lib.E_INVALID, name
+        assert "projection 1" in _lib.last_error(), name
+    # the same plan with another page table is accepted by validation; an all-idle batch
+    # then returns before any launch
+    idle = dict(seg_adapter=np.full_like(wl.seg_adapter, -1), token_adapter=np.full_like(wl.token_adapter, -1))
+    c3, _, _, _ = _call(wl, pool=pool, page_table_ptr=FAKE_DEV + 4096, **idle)
+    c4, _, _, _ = _call(wl, pool=pool, **idle)
+    assert _multi_code([c4, c3]) == 0
+
+
 def _even_split(toks, cap):
     n = len(toks)
     g = -(-n // cap)
@@ -326,4 +373,12 @@ def test_bench_accounting_follows_the_plan():
             assert a["mbgmv_fused"]["tokens"] == 0 and a["sgmv_fused"]["tokens"] == routed.size
         else:  # segments and hot adapters' ids on SGMV, ~360 singleton ids on MBGMV
             assert a["sgmv_fused"]["tokens"] > a["mbgmv_fused"]["tokens"] > 0
+        assert a["mixed_fused"]["bytes"] == a["mbgmv_fused"]["bytes"] + a["sgmv_fused"]["bytes"]
+        assert a["mixed_fused"]["mfma_flops"] == a["sgmv_fused"]["flops"]
         pool.destroy()
+    # a step's calls: same-shape runs of projections in one slora_apply_multi each
+    groups = {name: bench.projection_groups(workloads.make(name), True)
+              for name in ("decode_7b", "prefill_sgmv", "mixed_13b", "mlp_asym")}
+    assert groups == {"decode_7b": [[0]], "prefill_sgmv": [[0, 1, 2, 3]], "mixed_13b": [[0, 1, 2, 3]],
+                      "mlp_asym": [[0, 1], [2]]}
+    assert bench.projection_groups(workloads.make("prefill_sgmv"), False) == [[0], [1], [2], [3]]
