@@ -184,6 +184,34 @@ static void plan_round(std::mt19937_64& rng) {
     CHECK(slora_apply(&L, &R, xbad, kFakeDev, kFakeDev, 1 << 30, nullptr) == SLORA_E_INVALID);
     CHECK(slora_shrink(&L, &R, xbad, reinterpret_cast<float*>(kFakeDev), kFakeDev, 1 << 30,
                        nullptr) == SLORA_E_INVALID);
+    // several projections: one region per projection; projections that cannot share the
+    // plan, a misaligned x or a projection count outside 1..8 are refused up front
+    const int32_t n = 1 + (int32_t)(rng() % 8);
+    std::vector<slora_lora> Ls((size_t)n + 1, L);
+    std::vector<const void*> xs((size_t)n + 1, kFakeDev);
+    std::vector<void*> ys((size_t)n + 1, kFakeDev);
+    int64_t one = 0, multi = 0;
+    CHECK(slora_workspace_size(&L, &R, &one) == SLORA_OK);
+    CHECK(slora_workspace_size_multi(n, Ls.data(), &R, &multi) == SLORA_OK);
+    CHECK(multi == n * ((one + 255) / 256 * 256));
+    CHECK(slora_workspace_size_multi(9, Ls.data(), &R, &multi) == SLORA_E_INVALID);
+    xs[(size_t)(rng() % n)] = xbad;
+    CHECK(slora_apply_multi(n, Ls.data(), &R, xs.data(), ys.data(), kFakeDev, 1 << 30, nullptr) ==
+          SLORA_E_INVALID);
+    std::fill(xs.begin(), xs.end(), kFakeDev);
+    if (n > 1) {
+      std::vector<int64_t> base2(base);
+      std::vector<float> scale2(scale);
+      const int32_t q = 1 + (int32_t)(rng() % (n - 1));
+      switch (rng() % 3) {
+        case 0: Ls[(size_t)q].d_out = d_out + 8; break;
+        case 1: base2[(size_t)(rng() % n_ad)] += 1; Ls[(size_t)q].base = base2.data(); break;
+        default: scale2[(size_t)(rng() % n_ad)] = 2.f; Ls[(size_t)q].scale = scale2.data(); break;
+      }
+      CHECK(slora_apply_multi(n, Ls.data(), &R, xs.data(), ys.data(), kFakeDev, 1 << 30, nullptr) ==
+            SLORA_E_INVALID);
+      CHECK(std::strstr(slora_last_error(), "projection") != nullptr);
+    }
   }
 }
 
