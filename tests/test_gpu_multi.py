@@ -134,3 +134,44 @@ def test_mlp_multi_rank_classes(rt):
     say("[gpu] apply_multi mlp_asym gate+up, building instance")
     inst, _ = _multi_vs_single(rt, wl, projs=[wl.proj("gate")[0], wl.proj("up")[0]])
     inst.close()
+
+
+def test_multi_two_streams(rt):
+    """slora_apply_multi calls on two workspaces and two streams, issued alternately with
+    the host far ahead of the GPU: the library orders the launches across the streams,
+    every output is the same bits as the per-projection reference and both workspaces
+    report a clean status."""
+    from heterogeneous_lora_amd import _lib
+    wl = _small_multi(305, 4, dtype="f16", n_adapters=60, d_in=2048, d_out=2048, page_elems=1024,
+                      n_tokens=400, n_segments=4, rank_choices=(8, 16, 64, 128), p_none=0.05)
+    say("[gpu] apply_multi alternating over two streams, 4 projections")
+    inst = rt.PagedLoRA(wl)
+    calls = [inst.call(p) for p in range(4)]
+    ins = [inst.inputs(p) for p in range(4)]
+    single = []
+    for c, (x, y0) in zip(calls, ins):
+        y = y0.clone()
+        inst.apply(c, x, y, inst.workspace(c))
+        single.append(_bits(y))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.zeros(_lib.workspace_size_multi(calls), dtype=torch.uint8, device=inst.device)
+           for _ in range(2)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(20_000_000)  # bounded spin: the host runs ahead
+    outs = []
+    for i in range(8):
+        k = i % 2
+        with torch.cuda.stream(streams[k]):
+            ys = [y0.clone() for _, y0 in ins]
+            _lib.apply_multi(calls, [x.data_ptr() for x, _ in ins], [y.data_ptr() for y in ys],
+                             wss[k].data_ptr(), wss[k].numel(), streams[k].cuda_stream)
+        outs.append(ys)
+    torch.cuda.synchronize()
+    for k in range(2):
+        assert _lib.workspace_status(wss[k].data_ptr(), streams[k].cuda_stream) == 0
+    for i, ys in enumerate(outs):
+        for p in range(4):
+            assert np.array_equal(_bits(ys[p]), single[p]), (i, p)
+    inst.close()
