@@ -92,6 +92,17 @@ def test_small_multi_bit_identical(rt, name, kw, policy):
     inst.close()
 
 
+def test_multi_eight_projections(rt):
+    """The most projections one call takes (8), both families."""
+    wl = _small_multi(306, 8, dtype="bf16", n_adapters=30, d_in=768, d_out=1024, page_elems=256,
+                      n_tokens=160, n_segments=3, rank_choices=(4, 16, 96), p_none=0.05)
+    say("[gpu] apply_multi with 8 projections")
+    inst, ys = _multi_vs_single(rt, wl)
+    ref, _ = oracle_ref(wl, 7)
+    margin_line("apply_multi 8 projections, proj 7 all rows", check_close(_bits(ys[7]), ref, wl.dtype, "p7"))
+    inst.close()
+
+
 def test_multi_single_projection(rt):
     wl = _small_multi(304, 1, dtype="f16", n_adapters=20, d_in=512, d_out=512, page_elems=256,
                       n_tokens=90, n_segments=2, rank_choices=(8, 16, 128))
