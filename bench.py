@@ -369,7 +369,7 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     # HIP events recorded by the launch itself bracket every kernel of one step in
     # `event_every` (recording costs the host a few microseconds per launch, which would
     # otherwise pace the loop)
-    ev = max(1, event_every)
+    ev = max(1, min(event_every, steps // 4))  # and at least 4 timed steps
     t0 = time.perf_counter()
     for i in range(steps):
         if i % ev == 0:
