@@ -369,7 +369,7 @@ int slora_apply(const slora_lora* lora, const slora_routing* routing, const void
  * loras[0], and equal base, rank and scale arrays: the projections share the routing,
  * the adapters and the layout of their page tables (each its own page_table). A request's
  * adapter applies to every projection it adapts, and all adapter weights live in the one
- * pool (the S-LoRA overview, section "1. 统一分页"); running several projections in one
+ * pool (the S-LoRA overview, section "1. Unified Paging"); running several projections in one
  * launch is this library's own step, not one the pages give. A projection that differs
  * is refused with SLORA_E_INVALID before anything runs. The call plans once and runs the work of all
  * n_proj (1..8) projections in one launch (or two, when its segments get a launch per
