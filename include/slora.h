@@ -361,21 +361,21 @@ int slora_expand(const slora_lora* lora, const slora_routing* routing, const flo
 int slora_apply(const slora_lora* lora, const slora_routing* routing, const void* x, void* y,
                 void* ws, int64_t ws_bytes, void* stream);
 
-/* slora_apply over several projections of one batch at once (for instance a layer's
- * q, k, v and o): loras[p] describes projection p, which reads xs[p] (DEVICE
- * [n_tokens x d_in]) and updates ys[p] (DEVICE [n_tokens x d_out], y0 on entry) as
- * slora_apply would, with the same results bit for bit. Every loras[p] has the same
- * pool, n_pages, page_elems, dtype, d_in, d_out, n_adapters, r_max and page_table_len as
- * loras[0], and equal base, rank and scale arrays: the projections share the routing,
- * the adapters and the layout of their page tables (each its own page_table). A request's
- * adapter applies to every projection it adapts, and all adapter weights live in the one
- * pool (the S-LoRA overview, section "1. Unified Paging"); running several projections in one
+/* slora_apply over several projections of one batch at once (for instance a layer's q,
+ * k, v and o): loras[p] describes projection p, which reads xs[p] (DEVICE [n_tokens x
+ * d_in]) and updates ys[p] (DEVICE [n_tokens x d_out], y0 on entry) as slora_apply
+ * would, with the same results bit for bit. Every loras[p] has the same pool, n_pages,
+ * page_elems, dtype, d_in, d_out, n_adapters, r_max and page_table_len as loras[0], and
+ * equal base, rank and scale arrays: the projections share the routing, the adapters and
+ * the layout of their page tables (each its own page_table). A request's adapter applies
+ * to every projection it adapts, and all adapter weights live in the one pool (the
+ * S-LoRA overview, section "1. Unified Paging"); running several projections in one
  * launch is this library's own step, not one the pages give. A projection that differs
- * is refused with SLORA_E_INVALID before anything runs. The call plans once and runs the work of all
- * n_proj (1..8) projections in one launch (or two, when its segments get a launch per
- * rank class, as in slora_apply), which saves every launch's fixed ramp and tail but
- * one. ws: n_proj regions of slora_workspace_size_multi / n_proj bytes each, zero-filled
- * once; give-ups are read with slora_workspace_status(ws, ...). */
+ * is refused with SLORA_E_INVALID before anything runs. The call plans once and runs the
+ * work of all n_proj (1..8) projections in one launch (or two, when its segments get a
+ * launch per rank class, as in slora_apply), which saves every launch's fixed ramp and
+ * tail but one. ws: n_proj regions of slora_workspace_size_multi / n_proj bytes each,
+ * zero-filled once; give-ups are read with slora_workspace_status(ws, ...). */
 int slora_workspace_size_multi(int32_t n_proj, const slora_lora* loras, const slora_routing* routing,
                                int64_t* bytes);
 int slora_apply_multi(int32_t n_proj, const slora_lora* loras, const slora_routing* routing,
