@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the heterogeneous batched LoRA path on one MI355X.
 
-One step = one apply over every projection of the workload (plan on the host,
-work-list upload, shrink and expand kernels) for the whole token batch, adapters
-already resident in HBM. The default workload is the Llama-7B-shape decode batch:
+One step = one apply over every projection of the workload for the whole token
+batch (plan on the host into pinned memory, then the fused launches; a run of
+same-shape projections goes through one slora_apply_multi, --per-projection: one
+slora_apply each), adapters already resident in HBM. The default workload is the
+Llama-7B-shape decode batch:
 256 decode tokens, one 4096 -> 4096 projection, Zipf(1.0) routing over 1000
 adapters with ranks in {8, 16, 32, 64}, fp16.
 
@@ -17,8 +19,8 @@ plain device copy as a reachable-bandwidth reference, the CPU oracle's rate on t
 host cores, the adapter fetch rate beside a copy-engine host-to-device copy of the
 same bytes, and GPU / host facts. With the default decode workload the same line
 carries a `prefill` record: the prefill SGMV batch (64 requests, q/k/v/o 4096 ->
-4096, bf16) timed the same way, with HBM and MFMA fractions of both SGMV kernels.
-Every instance's workspace status is read after the timed steps; a decode launch
+4096, bf16) timed the same way, with the HBM and MFMA fractions of its launch.
+Every instance's workspace status is read after the timed steps; a fused launch
 whose wait gave up makes the run exit with status 3. Progress goes to stderr.
 """
 
@@ -75,6 +77,22 @@ def algorithmic(wl, proj, call):
     for f in ("sgmv_shrink", "sgmv_expand", "sgmv_fused", "mixed_fused"):
         out[f]["mfma_flops"] = out["sgmv_" + f.split("_")[1] if f.startswith("sgmv") else "sgmv_fused"]["flops"]
     return out
+
+
+def launch_work(alg, groups):
+    """Algorithmic [bytes, flops, matrix-core flops] of every timed interval a step has,
+    per kernel id, from the per-projection figures of algorithmic(): one interval per
+    projection and kernel id, except a slora_apply_multi's, which covers its group of
+    projections (both families in one interval, multi_fused)."""
+    per = {}
+    for g in groups:
+        if len(g) > 1:
+            fam = [sum(alg[p][f][q] for p in g for f in ("mbgmv_fused", "sgmv_fused")) for q in ("bytes", "flops")]
+            per.setdefault("multi_fused", []).append(fam + [sum(alg[p]["sgmv_fused"]["flops"] for p in g)])
+        else:
+            for k, a in alg[g[0]].items():
+                per.setdefault(k, []).append([a["bytes"], a["flops"], a.get("mfma_flops", 0)])
+    return per
 
 
 def projection_groups(wl, multi):
@@ -435,16 +453,7 @@ def run_workload(wl, policy, n_inst, steps, warmup, event_every, pct_steps, dev,
     value = T * steps / wall
     log(f"[bench] {steps} steps in {wall:.4f} s: {ms_per_step * 1e3:.1f} us/step, {value:.4g} tokens/s")
     alg = [algorithmic(wl, p, insts[0][1][p]) for p in range(n_proj)]
-    # algorithmic work per timed interval of each kernel id: one per projection, except a
-    # slora_apply_multi's, which covers its group of projections (both families)
-    per = {}
-    for g in groups:
-        if len(g) > 1:
-            fam = [sum(alg[p][f][q] for p in g for f in ("mbgmv_fused", "sgmv_fused")) for q in ("bytes", "flops")]
-            per.setdefault("multi_fused", []).append(fam + [sum(alg[p]["sgmv_fused"]["flops"] for p in g)])
-        else:
-            for k, a in alg[g[0]].items():
-                per.setdefault(k, []).append([a["bytes"], a["flops"], a.get("mfma_flops", 0)])
+    per = launch_work(alg, groups)
     kernels = {}
     for k in sorted(set(names)):
         d = np.array([m for n, m in zip(names, ms) if n == k])

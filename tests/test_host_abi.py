@@ -382,3 +382,16 @@ def test_bench_accounting_follows_the_plan():
     assert groups == {"decode_7b": [[0]], "prefill_sgmv": [[0, 1, 2, 3]], "mixed_13b": [[0, 1, 2, 3]],
                       "mlp_asym": [[0, 1], [2]]}
     assert bench.projection_groups(workloads.make("prefill_sgmv"), False) == [[0], [1], [2], [3]]
+    # a multi call's interval carries its projections' work, both families summed
+    wl = workloads.make("mixed_13b")
+    call, pool, pt, base = _call(wl)
+    a = bench.algorithmic(wl, 0, call)
+    alg = [a] * 4
+    per = bench.launch_work(alg, [[0, 1, 2, 3]])
+    assert list(per) == ["multi_fused"] and len(per["multi_fused"]) == 1
+    b, f, m = per["multi_fused"][0]
+    assert b == 4 * (a["mbgmv_fused"]["bytes"] + a["sgmv_fused"]["bytes"]) == 4 * a["mixed_fused"]["bytes"]
+    assert f == 4 * a["mixed_fused"]["flops"] and m == 4 * a["sgmv_fused"]["flops"]
+    single = bench.launch_work(alg, [[0], [1], [2], [3]])
+    assert len(single["mixed_fused"]) == 4 and single["mixed_fused"][0][0] == a["mixed_fused"]["bytes"]
+    pool.destroy()
