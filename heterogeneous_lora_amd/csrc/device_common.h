@@ -95,6 +95,44 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float c) {
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(uint16_t* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Read of a wave-uniform address through the scalar data cache (s_load). On a CU whose
+// waves keep many vector loads in flight, a new vector load queues behind them; a scalar
+// load reaches L2 on its own path. Only for memory that nothing writes while the kernel
+// runs (work lists, page tables): the scalar cache is not kept coherent within a launch.
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+// The same at a 32-bit byte offset from a base (the offset travels in one register).
+template <typename T>
+__device__ __forceinline__ T sload(const T* base, uint32_t byte_off) {
+  return *(const __attribute__((address_space(4))) T*)((const char*)base + byte_off);
+}
+
+// Makes the compiler issue all 16 scalar loads of `a` before this point and wait for them
+// once (it would otherwise wait for each load next to its use).
+__device__ __forceinline__ void settle16(int (&a)[16]) {
+  asm volatile(""
+               : "+s"(a[0]), "+s"(a[1]), "+s"(a[2]), "+s"(a[3]), "+s"(a[4]), "+s"(a[5]),
+                 "+s"(a[6]), "+s"(a[7]), "+s"(a[8]), "+s"(a[9]), "+s"(a[10]), "+s"(a[11]),
+                 "+s"(a[12]), "+s"(a[13]), "+s"(a[14]), "+s"(a[15]));
+}
+
+// 16 int32 entries base[min(first + i, last) * stride] (i < 16), read through the scalar
+// cache (every index wave-uniform, base[last * stride] in bounds), into lanes lane0 ..
+// lane0 + 15 of `into`: all loads are issued before one wait, and the values leave the
+// scalar registers right after.
+__device__ __forceinline__ int sload16_to_lanes(const int32_t* base, int first, int last,
+                                                int stride, int into, int lane0) {
+  int a[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = sload(base, (uint32_t)(min(first + i, last) * stride) * 4u);
+  settle16(a);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) into = (int)(threadIdx.x & 63) == lane0 + i ? a[i] : into;
+  return into;
+}
+
 // Sum V values per lane (V a power of two, 1..64) over the 64 lanes of a wave,
 // with no per-lane selects (which the compiler would turn into indexed scratch):
 //   * v_permlane32_swap pairs value i with value i + V/2 across the lane halves:

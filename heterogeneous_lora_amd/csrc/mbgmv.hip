@@ -55,8 +55,8 @@ __global__ __launch_bounds__(64 * kWaves) void mbgmv_kernel(
     Geom g, const MbItem* __restrict__ items, const uint16_t* __restrict__ x, void* v,
     uint16_t* __restrict__ y, uint32_t tag, unsigned long long* err, int32_t spin_limit) {
   extern __shared__ uint4 lds[];  // shrink: [G][kBatchVecs] of x; expand: partial sums
-  const MbItem it = items[blockIdx.x];
-  run_item<DT, kUniformChunk, kTag>(g, it, x, v, y, tag, err, spin_limit, lds);
+  const MbItem it = load_item(items, blockIdx.x);
+  run_item<DT, kUniformChunk, kTag, true>(g, it, x, v, y, tag, err, spin_limit, lds);
 }
 
 template <int DT, bool kTag>

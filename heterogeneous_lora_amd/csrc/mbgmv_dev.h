@@ -27,17 +27,25 @@ __device__ __forceinline__ int pick4(const int (&t)[kMbGroup], int i) {
 }
 
 // ------------------------------------------------------------------ shrink role
-template <int DT, bool kUniformChunk, int G, bool kTag>
+template <int DT, bool kUniformChunk, int G, bool kTag, bool kSgprIds>
 __device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
                                             const uint16_t* __restrict__ x, void* __restrict__ v,
                                             uint32_t tag, uint4* xs) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int k0 = it.part * kMbShrinkRows + wave * kRowsPerWave;
   const int nrow = max(0, min(kRowsPerWave, it.rank - k0));  // 0: this wave only stages x
   const int n = it.n_tok();
   const int nvec = g.d_in >> 3;
+  const int64_t pbase = (int64_t)it.pt_base + (int64_t)k0 * g.cA;
   const int npid = nrow * g.cA;  // <= 2 * 32 (the planner limits cA)
-  const int my_pid = lane < npid ? g.pt[(int64_t)it.pt_base + (int64_t)k0 * g.cA + lane] : -1;
+  int my_pid = -1;  // lane i: entry i of this wave's rows
+  if constexpr (kUniformChunk && kSgprIds) {
+    // read per batch into scalar registers instead (below)
+  } else if (kUniformChunk && npid <= 16) {  // scalar cache; no rows: the adapter's first entry
+    my_pid = sload16_to_lanes(g.pt + (npid > 0 ? pbase : (int64_t)it.pt_base), 0, max(npid - 1, 0), 1, -1, 0);
+  } else {
+    my_pid = lane < npid ? g.pt[pbase + lane] : -1;
+  }
   const int tok[kMbGroup] = {it.tok[0], it.tok[1], it.tok[2], it.tok[3]};
 
   float acc[kRowsPerWave][G];
@@ -48,6 +56,20 @@ __device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
 
   for (int vb = 0; vb < nvec; vb += kBatchVecs) {
     uint4 a[kRowsPerWave][kSlices];
+    int pg[kRowsPerWave * kSlices];  // kSgprIds: this batch's entries, all read before any is used
+    if constexpr (kUniformChunk && kSgprIds) {
+#pragma unroll
+      for (int u = 0; u < kSlices; ++u)
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) {
+          const int qb = vb + u * 64;
+          const bool live = qb < nvec && r < nrow;  // a dead row reads the adapter's first entry
+          pg[u * kRowsPerWave + r] =
+              sload(g.pt + (live ? pbase + r * g.cA + (qb * 8) / g.P : (int64_t)it.pt_base));
+        }
+      static_assert(kRowsPerWave * kSlices == 16, "settle16");
+      settle16(pg);
+    }
 #pragma unroll
     for (int u = 0; u < kSlices; ++u) {
       const int qb = vb + u * 64;  // first vector of this slice (uniform)
@@ -61,7 +83,7 @@ __device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
         const bool live = qb < nvec && r < nrow;  // uniform
         const int idx = live ? r * g.cA + c : 0;
         int page;
-        if constexpr (kUniformChunk) page = readlane(my_pid, idx);
+        if constexpr (kUniformChunk) page = kSgprIds ? pg[u * kRowsPerWave + r] : readlane(my_pid, idx);
         else page = __shfl(my_pid, idx);
         const bool ok = (uint32_t)page < (uint64_t)g.n_pages;
         a[r][u] = ld16(!live ? fill_zero() : ok ? g.pool + (int64_t)page * g.P + off : fill_nan<DT>());
@@ -115,12 +137,12 @@ __device__ __forceinline__ void shrink_body(const Geom& g, const MbItem& it,
 }
 
 // ------------------------------------------------------------------ expand role
-template <int DT, bool kUniformChunk, int NT, bool kTag>
+template <int DT, bool kUniformChunk, int NT, bool kTag, bool kSgprIds>
 __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
                                             const void* __restrict__ v, uint16_t* __restrict__ y,
                                             uint32_t tag, unsigned long long* err, int32_t spin_limit,
                                             float* red) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = it.rank, n = it.n_tok(), split = it.split();
   const int slices = kWaves / split, slice = wave / split, rp = wave % split;
   const int rpw = (r + split - 1) / split;  // rows per wave (<= 32)
@@ -134,8 +156,6 @@ __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
   else c = col / g.P;
   const int off = col - c * g.P;
   const int64_t pbase = (int64_t)it.pt_base + (int64_t)r * g.cA + c + (int64_t)k_lo * g.cB;
-  int pid = -1;  // lane k: page of this wave's row k_lo + k in its chunk (nk <= 32)
-  if constexpr (kUniformChunk) pid = lane < nk ? g.pt[pbase + (int64_t)lane * g.cB] : -1;
   const int t0 = it.tok[0], t1 = it.tok[1];
 
   uint4 y0v[NT];
@@ -143,14 +163,28 @@ __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
   for (int t = 0; t < NT; ++t)
     y0v[t] = ld16((rp == 0 && t < n && wave_live) ? y + (int64_t)(t ? t1 : t0) * g.d_out + col
                                                    : fill_zero());
+  int pid = -1;  // lane k: page of this wave's row k_lo + k in its chunk (nk <= 32)
+  if constexpr (kUniformChunk && !kSgprIds) {  // scalar cache; rows past nk repeat row nk - 1
+    const int32_t* pb = g.pt + (nk > 0 ? pbase : (int64_t)it.pt_base);  // no rows: first entry
+    pid = sload16_to_lanes(pb, 0, max(nk - 1, 0), g.cB, pid, 0);
+    if (nk > 16) pid = sload16_to_lanes(pb, 16, nk - 1, g.cB, pid, 16);
+  }
 
   auto load_rows = [&](uint4 (&b)[kKU], int k) {
+    int pg[kKU];  // kSgprIds: the batch's entries, all read before any is used
+    if constexpr (kUniformChunk && kSgprIds) {
+#pragma unroll
+      for (int u = 0; u < kKU; ++u)  // a dead row reads the adapter's first entry
+        pg[u] = sload(g.pt + (k + u < nk ? pbase + (int64_t)(k + u) * g.cB : (int64_t)it.pt_base));
+      static_assert(kKU == 16, "settle16");
+      settle16(pg);
+    }
 #pragma unroll
     for (int u = 0; u < kKU; ++u) {
       const int kk = k + u;
       const bool live = kk < nk && wave_live;  // uniform
       int page;
-      if constexpr (kUniformChunk) page = readlane(pid, kk & 63);
+      if constexpr (kUniformChunk) page = kSgprIds ? pg[u] : readlane(pid, kk & 63);
       else page = g.pt[live ? pbase + (int64_t)kk * g.cB : 0];
       const bool ok = (uint32_t)page < (uint64_t)g.n_pages;
       b[u] = ld16(!live ? fill_zero() : ok ? g.pool + (int64_t)page * g.P + off : fill_nan<DT>());
@@ -258,23 +292,40 @@ __device__ __forceinline__ void expand_body(const Geom& g, const MbItem& it,
   }
 }
 
+// A work item, read whole through the scalar cache (the list is not written while a
+// launch runs).
+__device__ __forceinline__ MbItem load_item(const MbItem* items, int64_t i) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(items + i);
+  uint32_t w[sizeof(MbItem) / 4];
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(MbItem) / 4); ++k) w[k] = sload(p + k);
+  MbItem it;
+  __builtin_memcpy(&it, w, sizeof(MbItem));
+  return it;
+}
+
 // Role per item. kTag: one fused call (v tagged, expand waves poll for it); otherwise a
 // shrink-only or expand-only launch with plain fp32 v. lds: the group's x (shrink,
 // [G][kBatchVecs] vectors) or the split waves' partial sums (expand, kRedBytes).
-template <int DT, bool kUniformChunk, bool kTag>
+// Page-table entries of uniform-chunk geometries come through the scalar cache, 16 per
+// wave and batch with one wait. kSgprIds: they stay in scalar registers and address the
+// rows directly (the MBGMV kernel; a wave issues its rows soonest); otherwise they move
+// to lanes of one vector register and are read back per row (the launch that also runs
+// segment tiles, whose register budget the extra scalar registers would spill into).
+template <int DT, bool kUniformChunk, bool kTag, bool kSgprIds>
 __device__ __forceinline__ void run_item(const Geom& g, const MbItem& it, const uint16_t* x,
                                          void* v, uint16_t* y, uint32_t tag,
                                          unsigned long long* err, int32_t spin_limit, uint4* lds) {
   if (it.role() == 0) {
     const int n = it.n_tok();
     static_assert(kMbGroup == 4, "shrink bodies cover 1, 2 and 4 tokens");
-    if (n <= 1) shrink_body<DT, kUniformChunk, 1, kTag>(g, it, x, v, tag, lds);
-    else if (n <= 2) shrink_body<DT, kUniformChunk, 2, kTag>(g, it, x, v, tag, lds);
-    else shrink_body<DT, kUniformChunk, 4, kTag>(g, it, x, v, tag, lds);
+    if (n <= 1) shrink_body<DT, kUniformChunk, 1, kTag, kSgprIds>(g, it, x, v, tag, lds);
+    else if (n <= 2) shrink_body<DT, kUniformChunk, 2, kTag, kSgprIds>(g, it, x, v, tag, lds);
+    else shrink_body<DT, kUniformChunk, 4, kTag, kSgprIds>(g, it, x, v, tag, lds);
   } else {
     float* red = reinterpret_cast<float*>(lds);
-    if (it.n_tok() <= 1) expand_body<DT, kUniformChunk, 1, kTag>(g, it, v, y, tag, err, spin_limit, red);
-    else expand_body<DT, kUniformChunk, 2, kTag>(g, it, v, y, tag, err, spin_limit, red);
+    if (it.n_tok() <= 1) expand_body<DT, kUniformChunk, 1, kTag, kSgprIds>(g, it, v, y, tag, err, spin_limit, red);
+    else expand_body<DT, kUniformChunk, 2, kTag, kSgprIds>(g, it, v, y, tag, err, spin_limit, red);
   }
 }
 

@@ -686,8 +686,8 @@ __global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void mixed_fuse
   const uint16_t* x = static_cast<const uint16_t*>(io.x);
   uint16_t* y = static_cast<uint16_t*>(io.y);
   if (part == 0 || part == 2) {
-    const MbItem it = items[part == 0 ? i : a + i];
-    mb::run_item<DT, kUniformChunk, true>(gp, it, x, io.v_mb, y, tag, err, spin_limit, lds);
+    const MbItem it = mb::load_item(items, part == 0 ? i : a + i);
+    mb::run_item<DT, kUniformChunk, true, false>(gp, it, x, io.v_mb, y, tag, err, spin_limit, lds);
     return;
   }
   SgWork wp = w;
