@@ -650,7 +650,10 @@ __global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void sgmv_fused
 // has one launch instead of two; a call over several projections of one batch (same
 // routing and adapters, one page table, x, y and workspace region each) runs all of
 // them in that launch too. Workgroups: [MBGMV shrink items][segment shrink items]
-// [MBGMV expand items][segment expand items], each part projection-major. Every shrink
+// [MBGMV expand items][segment expand items]; inside a part the projections take turns
+// item by item, so the launch runs every projection's costliest items (groups and tiles
+// come by descending rank) before any projection's cheapest, and its tail is short
+// (item i of projection p is workgroup part_start + i * n_proj + p). Every shrink
 // item of either family and any projection comes before every expand item and none
 // waits, so the in-order-dispatch argument holds for every hand-off (v words for
 // MBGMV, flags for the segments, each in its projection's workspace region); they
@@ -670,15 +673,14 @@ __global__ __launch_bounds__(64 * kWaves, fused_waves(NBM, KBM)) void mixed_fuse
   const int a = n_mb_shrink, b = sg_shrink_items<NBM, KBM>(w), c = n_mb - n_mb_shrink;
   int L = (int)blockIdx.x, part, p, i;
   if (L < n_proj * a) {
-    part = 0, p = L / a, i = L % a;
+    part = 0, p = L % n_proj, i = L / n_proj;
   } else if ((L -= n_proj * a) < n_proj * b) {
-    part = 1, p = L / b, i = L % b;
+    part = 1, p = L % n_proj, i = L / n_proj;
   } else if ((L -= n_proj * b) < n_proj * c) {
-    part = 2, p = L / c, i = L % c;
+    part = 2, p = L % n_proj, i = L / n_proj;
   } else {
     L -= n_proj * c;
-    const int d = w.n_tiles * sg_expand_blocks(g);
-    part = 3, p = L / d, i = L % d;
+    part = 3, p = L % n_proj, i = L / n_proj;
   }
   const ProjIO io = pr.p[p];
   Geom gp = g;
