@@ -463,7 +463,7 @@ int launch_multi(int32_t n, const slora_lora* Ls, const slora_routing* R, const 
   int rc = order_fused(*ring, s);
   if (rc) return rc;
   const int32_t v_stride = sg_v_stride(L->r_max);
-  const SgSplit sp = pv.n_sg ? sg_split(L->d_in, pv.n_sg, sgmv_shrink_resident(pv.sg_max_rank, L->dtype))
+  const SgSplit sp = pv.n_sg ? sg_split(L->d_in, pv.n_sg, sgmv_shrink_resident(pv.sg_max_rank, L->dtype), n)
                              : SgSplit{};
   const int64_t part_stride = (int64_t)R->n_tokens * v_stride;
   ProjIO io[kMaxProj], io2[kMaxProj];

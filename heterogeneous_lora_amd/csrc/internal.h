@@ -169,11 +169,12 @@ hipError_t launch_zero(void* p, int64_t bytes, hipStream_t s);
 // SGMV shrink over ksplit (<= kSgMaxSplit) k-ranges of kc (a multiple of 128)
 // elements: range ks writes its partial sums to vpart + ks * split_stride, rows of
 // v_stride floats per token. The expand adds the ksplit partials in range order.
-// slots: shrink workgroups the device holds at once (sgmv_shrink_resident).
+// slots: shrink workgroups the device holds at once (sgmv_shrink_resident); n_proj:
+// projections whose tiles the launch runs.
 struct SgSplit {
   int32_t ksplit, kc;
 };
-SgSplit sg_split(int32_t d_in, int32_t n_tiles, int32_t slots);
+SgSplit sg_split(int32_t d_in, int32_t n_tiles, int32_t slots, int32_t n_proj = 1);
 // Workgroups of the shrink template for ranks up to max_rank that fit on the current
 // device at once (0 if the runtime cannot say).
 int sgmv_shrink_resident(int32_t max_rank, int32_t dtype);

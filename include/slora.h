@@ -364,7 +364,14 @@ int slora_apply(const slora_lora* lora, const slora_routing* routing, const void
 /* slora_apply over several projections of one batch at once (for instance a layer's q,
  * k, v and o): loras[p] describes projection p, which reads xs[p] (DEVICE [n_tokens x
  * d_in]) and updates ys[p] (DEVICE [n_tokens x d_out], y0 on entry) as slora_apply
- * would, with the same results bit for bit. Every loras[p] has the same pool, n_pages,
+ * would. The results are slora_apply's bit for bit for decode groups and for one
+ * projection; with segment tiles and several projections the launch may split the
+ * segment shrink into fewer k-ranges (its other projections' work fills the device), so
+ * the same fp32 terms are added in another grouping and outputs agree with
+ * slora_apply's to rounding (the intermediate v, which the segment expand reads in the
+ * storage type, can round the other way, and y's own rounding can then land one unit
+ * away). Repeated calls give the same bits.
+ * Every loras[p] has the same pool, n_pages,
  * page_elems, dtype, d_in, d_out, n_adapters, r_max and page_table_len as loras[0], and
  * equal base, rank and scale arrays: the projections share the routing, the adapters and
  * the layout of their page tables (each its own page_table). A request's adapter applies

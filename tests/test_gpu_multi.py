@@ -1,8 +1,12 @@
 """GPU tests of slora_apply_multi (several projections of one batch in one launch),
-through the C ABI: every projection's output is bit-identical to what slora_apply gives
-for that projection alone (the same items run the same arithmetic, only in one launch),
-the workspace status is clean, and one projection set is also checked against the
-oracle. Each case names itself on stderr before it touches the GPU."""
+through the C ABI: every projection's output equals what slora_apply gives for that
+projection alone, bit for bit where the two calls split the segment shrink into the same
+k-ranges (one projection, decode groups only) and otherwise to rounding (_assert_same
+states the bound); repeated calls give the same bits, the workspace status is clean, and
+one projection of each case is also checked against the oracle. A multi-projection
+launch may split the segment shrink into fewer k-ranges than a one-projection launch, so
+the same fp32 terms are added in another grouping. Each case names itself on stderr
+before it touches the GPU."""
 
 import dataclasses
 
@@ -29,10 +33,40 @@ def _bits(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def _multi_vs_single(rt, wl, projs=None, policy=0, launches=("multi_fused",), inst=None):
+def _decode(bits, dtype):
+    bits = np.asarray(bits).view(np.uint16)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _assert_same(got, want, dtype, exact, what):
+    """got == want bit for bit (exact); else, element by element,
+    |got - want| <= ulp(want) + 2^-12 * max(1, max|want|). The two differ by how the
+    same fp32 terms are grouped (a relative 2^-22 or so), by v entries that the segment
+    expand reads rounded to the storage type and that round the other way (a shift of
+    about 1e-5 at these value scales, far below 2^-12), and by the final rounding of y,
+    which can then land one unit away. A wrong row, column or projection moves an
+    output by the size of the LoRA term (~5e-2 here) and fails."""
+    if exact:
+        assert np.array_equal(got, want), what
+        return
+    g, w = _decode(got, dtype), _decode(want, dtype)
+    wb = np.asarray(want).view(np.uint16)
+    nxt = ((wb & 0x8000) | ((wb & 0x7FFF) + 1)).astype(np.uint16)  # next value away from 0
+    ulp = np.abs(_decode(nxt, dtype) - w)
+    bound = ulp + 2.0 ** -12 * max(1.0, float(np.abs(w).max(initial=0.0)))
+    excess = np.abs(g - w) - bound
+    assert float(excess.max(initial=-1.0)) <= 0.0, (what, float(np.abs(g - w).max()),
+                                                     int((got != want).sum()))
+
+
+def _multi_vs_single(rt, wl, projs=None, policy=0, launches=("multi_fused",), inst=None, exact=None):
     """Runs the projections one by one with slora_apply, then all at once with
     slora_apply_multi (twice: the second call finds the first call's flags and v words
-    in the workspace), and requires the same bits. Returns (instance, multi outputs)."""
+    in the workspace), and requires the same outputs: bit for bit when `exact` (by
+    default, for a single projection), else within one unit in the last place. Both
+    multi calls must give the same bits. Returns (instance, multi outputs)."""
     from heterogeneous_lora_amd import _lib
     inst = inst or rt.PagedLoRA(wl)
     projs = list(range(len(wl.projections))) if projs is None else projs
@@ -45,7 +79,10 @@ def _multi_vs_single(rt, wl, projs=None, policy=0, launches=("multi_fused",), in
         ws = inst.workspace(c)
         inst.apply(c, x, y, ws)
         single.append(_bits(y))
+    if exact is None:
+        exact = len(projs) == 1
     ws = torch.zeros(_lib.workspace_size_multi(calls), dtype=torch.uint8, device=inst.device)
+    first = None
     for rep in range(2):
         ys = [y0.clone() for _, y0 in ins]
         _lib.timing_enable(True)
@@ -55,8 +92,14 @@ def _multi_vs_single(rt, wl, projs=None, policy=0, launches=("multi_fused",), in
         names, _ = _lib.timing_read_all()
         assert names == list(launches), names
         assert _lib.workspace_status(ws.data_ptr(), stream) == 0
+        got = [_bits(y) for y in ys]
         for i, p in enumerate(projs):
-            assert np.array_equal(_bits(ys[i]), single[i]), (wl.name, p, rep)
+            _assert_same(got[i], single[i], wl.dtype, exact, (wl.name, p, rep))
+        if first is None:
+            first = got
+        else:
+            for i in range(len(projs)):
+                assert np.array_equal(got[i], first[i]), (wl.name, projs[i], "repeat")
     return inst, ys
 
 
@@ -86,7 +129,7 @@ SMALL = [
 def test_small_multi_bit_identical(rt, name, kw, policy):
     wl = _small_multi(kw["seed"], 3, **{k: v for k, v in kw.items() if k != "seed"})
     say(f"[gpu] apply_multi small {name}: 3 projections {wl.projections[0].d_in}x{wl.projections[0].d_out}")
-    inst, ys = _multi_vs_single(rt, wl, policy=policy)
+    inst, ys = _multi_vs_single(rt, wl, policy=policy, exact=(name == "decode"))
     ref, _ = oracle_ref(wl, 2)
     margin_line(f"apply_multi small {name} proj 2 all rows", check_close(_bits(ys[2]), ref, wl.dtype, name))
     inst.close()
@@ -184,5 +227,6 @@ def test_multi_two_streams(rt):
         assert _lib.workspace_status(wss[k].data_ptr(), streams[k].cuda_stream) == 0
     for i, ys in enumerate(outs):
         for p in range(4):
-            assert np.array_equal(_bits(ys[p]), single[p]), (i, p)
+            _assert_same(_bits(ys[p]), single[p], wl.dtype, False, (i, p))
+            assert np.array_equal(_bits(ys[p]), _bits(outs[0][p])), (i, p, "repeat")
     inst.close()
