@@ -113,7 +113,7 @@ constexpr int kSegs = kBatch / 8;  // 16-byte segments per slab row
 constexpr int shrink_waves(int nb) { return nb <= 4 ? 4 : 1; }
 constexpr int expand_waves(int kb) { return kb <= 1 ? 4 : 3; }
 constexpr int32_t kSgMinSplit = 3;       // k-ranges at least, one projection per launch
-constexpr int32_t kSgMinSplitMulti = 2;  // the same, several projections in one launch
+constexpr int32_t kSgMinSplitMulti = 1;  // the same, several projections in one launch
 // 16-row blocks of rank rows the shrink template for ranks up to max_rank holds.
 constexpr int shrink_nb(int max_rank) { return max_rank <= 16 ? 1 : max_rank <= 32 ? 2 : max_rank <= 64 ? 4 : 8; }
 
@@ -869,11 +869,11 @@ SgSplit sg_split(int32_t d_in, int32_t n_tiles, int32_t slots, int32_t n_proj) {
   // expand reads every range's partial sums. With one projection per launch, three
   // ranges measured best on the prefill batch (290 tiles), the MLP batch (~480 tiles)
   // and the mixed batch (~130 tiles, ranks to 128); with several projections in one
-  // launch, whose other projections' items fill the tail of a short round, two (the
-  // same three batches' multi-projection launches, 1.5-2.6% faster than with three).
-  // More are used only while every (tile, k-range) workgroup of the launch still fits
-  // on the device at once, since a launch that spills a little into a second round
-  // ends with a tail of lone chains.
+  // launch, whose other projections' items fill the tail of a short round, one (the
+  // prefill and mixed batches' four-projection launches 2-4% faster than with three,
+  // the MLP batch's two-projection launch within 1%). More are used only while every
+  // (tile, k-range) workgroup of the launch still fits on the device at once, since a
+  // launch that spills a little into a second round ends with a tail of lone chains.
   const int32_t items = n_tiles * std::max(n_proj, 1);
   const int32_t ks_min = n_proj > 1 ? kSgMinSplitMulti : kSgMinSplit;
   int32_t ks = n_tiles > 0 ? std::max(ks_min, slots / items) : 1;
