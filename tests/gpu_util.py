@@ -32,6 +32,25 @@ def check_close(y_gpu_bits, y_ref, dtype, what=""):
     return err / scale
 
 
+def assert_same_to_rounding(got, want, dtype, what=""):
+    """Two GPU results of one computation whose fp32 sums were grouped differently, as
+    storage-type bit patterns, element by element:
+    |got - want| <= ulp(want) + 2^-12 * max(1, max|want|). The grouping moves an fp32 sum
+    by a relative 2^-22 or so; v entries that the segment expand reads rounded to the
+    storage type can round the other way, which moves y by about 1e-5 at the workloads'
+    value scales (far below 2^-12); y's own rounding can then land one unit away. A wrong
+    row, column or projection moves an output by the size of the LoRA term (~5e-2) and
+    fails."""
+    g, w = decode(got, dtype), decode(want, dtype)
+    wb = np.asarray(want).view(np.uint16)
+    nxt = ((wb & 0x8000) | ((wb & 0x7FFF) + 1)).astype(np.uint16)  # next value away from 0
+    ulp = np.abs(decode(nxt, dtype) - w)
+    bound = ulp + 2.0 ** -12 * max(1.0, float(np.abs(w).max(initial=0.0)))
+    excess = np.abs(g - w) - bound
+    assert float(excess.max(initial=-1.0)) <= 0.0, (what, float(np.abs(g - w).max()),
+                                                     int((np.asarray(got) != np.asarray(want)).sum()))
+
+
 def margin_line(what, rel):
     """One greppable line per parity check: max|y - y_ref| / max(1, ||y_ref||_inf) and the
     tolerance, so the margins of every workload and routing policy are on record."""

@@ -1,12 +1,12 @@
 """GPU tests of slora_apply_multi (several projections of one batch in one launch),
 through the C ABI: every projection's output equals what slora_apply gives for that
 projection alone, bit for bit where the two calls split the segment shrink into the same
-k-ranges (one projection, decode groups only) and otherwise to rounding (_assert_same
-states the bound); repeated calls give the same bits, the workspace status is clean, and
-one projection of each case is also checked against the oracle. A multi-projection
-launch may split the segment shrink into fewer k-ranges than a one-projection launch, so
-the same fp32 terms are added in another grouping. Each case names itself on stderr
-before it touches the GPU."""
+k-ranges (one projection, decode groups only) and otherwise to rounding (the bound is
+stated in gpu_util.assert_same_to_rounding); repeated calls give the same bits, the
+workspace status is clean, and one projection of each case is also checked against the
+oracle. A multi-projection launch may split the segment shrink into fewer k-ranges than
+a one-projection launch, so the same fp32 terms are added in another grouping. Each
+case names itself on stderr before it touches the GPU."""
 
 import dataclasses
 
@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import check_close, margin_line, oracle_ref, sample_tokens, say
+from gpu_util import assert_same_to_rounding, check_close, margin_line, oracle_ref, sample_tokens, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -33,32 +33,12 @@ def _bits(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def _decode(bits, dtype):
-    bits = np.asarray(bits).view(np.uint16)
-    if dtype == "f16":
-        return bits.view(np.float16).astype(np.float64)
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
 def _assert_same(got, want, dtype, exact, what):
-    """got == want bit for bit (exact); else, element by element,
-    |got - want| <= ulp(want) + 2^-12 * max(1, max|want|). The two differ by how the
-    same fp32 terms are grouped (a relative 2^-22 or so), by v entries that the segment
-    expand reads rounded to the storage type and that round the other way (a shift of
-    about 1e-5 at these value scales, far below 2^-12), and by the final rounding of y,
-    which can then land one unit away. A wrong row, column or projection moves an
-    output by the size of the LoRA term (~5e-2 here) and fails."""
+    """got == want bit for bit (exact), else to rounding (assert_same_to_rounding)."""
     if exact:
         assert np.array_equal(got, want), what
-        return
-    g, w = _decode(got, dtype), _decode(want, dtype)
-    wb = np.asarray(want).view(np.uint16)
-    nxt = ((wb & 0x8000) | ((wb & 0x7FFF) + 1)).astype(np.uint16)  # next value away from 0
-    ulp = np.abs(_decode(nxt, dtype) - w)
-    bound = ulp + 2.0 ** -12 * max(1.0, float(np.abs(w).max(initial=0.0)))
-    excess = np.abs(g - w) - bound
-    assert float(excess.max(initial=-1.0)) <= 0.0, (what, float(np.abs(g - w).max()),
-                                                     int((got != want).sum()))
+    else:
+        assert_same_to_rounding(got, want, dtype, what)
 
 
 def _multi_vs_single(rt, wl, projs=None, policy=0, launches=("multi_fused",), inst=None, exact=None):
