@@ -14,9 +14,10 @@
 //     page table) are both contiguous in j, so both operands are plain 16-byte
 //     loads. Each wave owns 16 tokens and reads its x rows straight from global
 //     memory; the A^T rows, which all 4 waves need, pass through LDS once per
-//     workgroup. The k-ranges give the launch enough workgroups to fill the chip
-//     without spilling into a second round; the expand adds the ranges' partial
-//     sums in range order, so the result does not depend on scheduling.
+//     workgroup. The k-ranges give a launch of one projection enough workgroups to
+//     fill the chip without spilling into a second round (a launch of several
+//     projections has enough without them: sg_split); the expand adds the ranges'
+//     partial sums in range order, so the result does not depend on scheduling.
 //   expand (tile, 1024 output columns): y[t, n] = RNE(y0 + s * sum_k v[t, k] B[k, n]).
 //     The product is computed transposed, D = B^T v^T, so that each lane ends up
 //     with 8 consecutive output columns of one token (16-byte y0 loads and y
